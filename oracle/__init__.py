@@ -1,0 +1,195 @@
+"""CPU oracle for the DSA decode path (test infrastructure only).
+
+Only the tests, `__graft_entry__.smoke()` and the `cpu_baseline` leg of
+`bench.py` may import this package. The product path (the HIP library and its
+Python binding) never imports, links or calls it.
+
+The arithmetic lives in plain C (`dsa_oracle.c`, IEEE double precision); this
+module only marshals numpy arrays through ctypes. `build()` compiles the C file
+with gcc into `liboracle.so` next to it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "dsa_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
+    lib = ctypes.CDLL(LIB)
+    P = ctypes.c_void_p
+    i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = dbl
+    lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3fn_to_f64.restype = dbl
+    lib.oracle_index_scores.argtypes = [i32, i32, i32, i32, P, P, P, i64, P, i64, P]
+    lib.oracle_index_scores.restype = i32
+    lib.oracle_topk_row.argtypes = [i64, i64, P, P]
+    lib.oracle_topk_row.restype = i32
+    lib.oracle_topk.argtypes = [i32, i64, i64, P, P, P]
+    lib.oracle_topk.restype = i32
+    lib.oracle_mla_decode.argtypes = [i32, i32, i32, i32, P, P, i64, i32, P, i64, P, P, i64,
+                                      dbl, dbl, P]
+    lib.oracle_mla_decode.restype = i32
+    lib.oracle_softmax_weights.argtypes = [i32, i32, i32, i32, i32, P, P, i64, i32, P, i64, P,
+                                           P, i64, dbl, dbl, P]
+    lib.oracle_softmax_weights.restype = i32
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise OracleError(f"{what} failed with code {rc}")
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def bf16_to_f64(code: int) -> float:
+    return float(_load().oracle_bf16_to_f64(int(code)))
+
+
+def e4m3_to_f64(code: int) -> float:
+    return float(_load().oracle_e4m3fn_to_f64(int(code)))
+
+
+def index_scores(q_idx, w, k_normed, seq_lens, rows_per_seq: int = 1,
+                 max_len: Optional[int] = None) -> np.ndarray:
+    """scores [R, max_len] float64; q_idx [R,Hi,D] bf16 codes, w [R,Hi] f32,
+    k_normed [S,cap,D] bf16 codes, seq_lens [R]."""
+    q_idx = _c(q_idx, np.uint16)
+    w = _c(w, np.float32)
+    k_normed = _c(k_normed, np.uint16)
+    seq_lens = _c(seq_lens, np.int32)
+    R, Hi, D = q_idx.shape
+    cap = k_normed.shape[1]
+    if max_len is None:
+        max_len = int(seq_lens.max()) if R else 0
+    out = np.zeros((R, max_len), dtype=np.float64)
+    rc = _load().oracle_index_scores(R, rows_per_seq, Hi, D, _p(q_idx), _p(w), _p(k_normed),
+                                     cap, _p(seq_lens), max_len, _p(out))
+    _check(rc, "oracle_index_scores")
+    return out
+
+
+def topk_row(scores_row, L: int, top_k: int) -> np.ndarray:
+    s = _c(scores_row, np.float64)
+    assert s.shape[0] >= L
+    sel = np.empty(top_k, dtype=np.int32)
+    _check(_load().oracle_topk_row(L, top_k, _p(s), _p(sel)), "oracle_topk_row")
+    return sel
+
+
+def topk(scores, seq_lens, top_k: int) -> np.ndarray:
+    """sel [R, top_k] int32: ascending selected ids, -1 padded. `scores` may be
+    float32 (the GPU's) or float64; float32 widens to float64 exactly."""
+    s = _c(scores, np.float64)
+    seq_lens = _c(seq_lens, np.int32)
+    R, max_len = s.shape
+    sel = np.empty((R, top_k), dtype=np.int32)
+    _check(_load().oracle_topk(R, max_len, top_k, _p(s), _p(seq_lens), _p(sel)), "oracle_topk")
+    return sel
+
+
+def mla_decode(q, kv_cache, block_tables, seq_lens, sel, kv_scale: float, sm_scale: float,
+               rows_per_seq: int = 1) -> np.ndarray:
+    """out [R, H, Dl] float64."""
+    q = _c(q, np.uint16)
+    kv_cache = _c(kv_cache, np.uint8)
+    block_tables = _c(block_tables, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    sel = _c(sel, np.int32)
+    R, H, Dl = q.shape
+    num_pages, ps, Dl2 = kv_cache.shape
+    assert Dl2 == Dl
+    top_k = sel.shape[1]
+    out = np.zeros((R, H, Dl), dtype=np.float64)
+    rc = _load().oracle_mla_decode(R, rows_per_seq, H, Dl, _p(q), _p(kv_cache), num_pages, ps,
+                                   _p(block_tables), block_tables.shape[1], _p(seq_lens),
+                                   _p(sel), top_k, float(kv_scale), float(sm_scale), _p(out))
+    _check(rc, "oracle_mla_decode")
+    return out
+
+
+def softmax_weights(q, kv_cache, block_tables, seq_lens, sel, kv_scale: float,
+                    sm_scale: float, r: int, h: int, rows_per_seq: int = 1) -> np.ndarray:
+    q = _c(q, np.uint16)
+    kv_cache = _c(kv_cache, np.uint8)
+    block_tables = _c(block_tables, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    sel = _c(sel, np.int32)
+    R, H, Dl = q.shape
+    num_pages, ps, _ = kv_cache.shape
+    top_k = sel.shape[1]
+    n = min(top_k, int(seq_lens[r]))
+    p = np.zeros(max(n, 1), dtype=np.float64)
+    rc = _load().oracle_softmax_weights(rows_per_seq, H, Dl, r, h, _p(q), _p(kv_cache),
+                                        num_pages, ps, _p(block_tables), block_tables.shape[1],
+                                        _p(seq_lens), _p(sel), top_k, float(kv_scale),
+                                        float(sm_scale), _p(p))
+    _check(rc, "oracle_softmax_weights")
+    return p[:n]
+
+
+def decode(inputs: dict, rows=None):
+    """End to end on the oracle alone: its own scores, its own selection, its
+    own attention. `rows` restricts the work to a subset of rows (all of a
+    row's inputs are sliced; sequences are looked up through r // K)."""
+    K = inputs["rows_per_seq"]
+    R = inputs["seq_lens"].shape[0]
+    rows = list(range(R)) if rows is None else list(rows)
+    out_scores, out_sel, out_att = [], [], []
+    for r in rows:
+        s = r // K
+        sl = inputs["seq_lens"][r:r + 1]
+        sc = index_scores(inputs["q_idx"][r:r + 1], inputs["w"][r:r + 1],
+                          inputs["k_normed"][s:s + 1], sl, 1, int(sl[0]))
+        se = topk(sc, sl, inputs["top_k"])
+        at = mla_decode(inputs["q"][r:r + 1], inputs["kv_cache"],
+                        inputs["block_tables"][s:s + 1], sl, se,
+                        inputs["kv_scale"], inputs["sm_scale"], 1)
+        out_scores.append(sc[0])
+        out_sel.append(se[0])
+        out_att.append(at[0])
+    return out_scores, np.stack(out_sel), np.stack(out_att)

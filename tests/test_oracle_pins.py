@@ -1,0 +1,308 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself
+(the published number formats through torch's casts, hand-worked examples,
+closed forms, brute force over all subsets, dense attention, invariants)."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_03_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(x):
+    return wl.f32_to_bf16_codes(np.asarray(x, dtype=np.float32))
+
+
+def e4m3(x):
+    return wl.f32_to_e4m3_codes(np.asarray(x, dtype=np.float32))
+
+
+def torch_e4m3_table():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- formats
+
+def test_bf16_decode_matches_torch_on_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_f64(c) for c in codes[::7]])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref[::7]))
+    ok = ~np.isnan(ref[::7])
+    np.testing.assert_array_equal(got[ok], ref[::7][ok])
+    # and every code of the exponent-boundary region exactly
+    for c in list(range(0, 0x90)) + list(range(0x7F00, 0x8090)) + list(range(0xFF00, 0x10000)):
+        r = ref[c]
+        g = oracle.bf16_to_f64(c)
+        assert (math.isnan(r) and math.isnan(g)) or (g == r and math.copysign(1, g) == math.copysign(1, r))
+
+
+def test_e4m3_decode_matches_torch_on_all_256_codes():
+    ref = torch_e4m3_table()
+    got = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    assert np.isnan(got).sum() == 2 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_decode_matches_ocp_spec_values():
+    g = json.load(open(os.path.join(GOLDEN, "e4m3_ocp_values.json")))
+    for code, val in g["values"].items():
+        got = oracle.e4m3_to_f64(int(code, 16))
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    for code in g["nan_codes"]:
+        assert math.isnan(oracle.e4m3_to_f64(int(code, 16)))
+
+
+def test_generator_e4m3_encode_is_nearest_and_saturating():
+    table = torch_e4m3_table()
+    finite = np.where(~np.isnan(table))[0]
+    vals = table[finite]
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(4000) * 40, [500.0, -1e4, 448.0, 464.0, 2.0 ** -10]])
+    codes = e4m3(x)
+    dec = table[codes]
+    assert not np.isnan(dec).any()
+    for xi, di in zip(x.astype(np.float32).astype(np.float64), dec):
+        xc = min(max(xi, -448.0), 448.0)
+        best = np.min(np.abs(vals - xc))
+        assert abs(di - xc) == best
+
+
+# ---------------------------------------------------------------- scores
+
+def test_scores_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "index_scores_worked.json")))
+    q = bf16(np.array(g["q_idx"])[None])
+    w = np.array(g["w"], dtype=np.float32)[None]
+    k = bf16(np.array(g["keys"])[None])
+    sl = np.array([len(g["keys"])], dtype=np.int32)
+    sc = oracle.index_scores(q, w, k, sl)
+    np.testing.assert_array_equal(sc[0], g["expected_scores"])
+
+
+def test_scores_one_hot_keys_pick_a_query_column():
+    rng = np.random.default_rng(1)
+    Hi, D = 5, 16
+    qf = rng.standard_normal((1, Hi, D)).astype(np.float32)
+    q = bf16(qf)
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double().numpy()
+    w = rng.random((1, Hi)).astype(np.float32)
+    keys = np.eye(D, dtype=np.float32)[None]
+    sc = oracle.index_scores(q, w, bf16(keys), np.array([D], np.int32))
+    expect = (w[0].astype(np.float64)[:, None] * np.maximum(qd[0], 0.0)).sum(axis=0)
+    np.testing.assert_allclose(sc[0], expect, rtol=1e-15, atol=0)
+
+
+def test_scores_single_head_unit_weight_is_relu_of_dot():
+    rng = np.random.default_rng(2)
+    D, L = 64, 50
+    q = bf16(rng.standard_normal((1, 1, D)))
+    k = bf16(rng.standard_normal((1, L, D)))
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double().numpy()[0, 0]
+    kd = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).double().numpy()[0]
+    sc = oracle.index_scores(q, np.ones((1, 1), np.float32), k, np.array([L], np.int32))
+    expect = np.maximum(kd @ qd, 0.0)
+    assert (expect == 0).sum() > 5 and (expect > 0).sum() > 5
+    np.testing.assert_allclose(sc[0], expect, rtol=1e-13, atol=1e-13)
+
+
+def test_scores_linear_in_weights_and_homogeneous_in_keys():
+    rng = np.random.default_rng(3)
+    Hi, D, L = 4, 32, 40
+    q = bf16(rng.standard_normal((1, Hi, D)))
+    kf = rng.standard_normal((1, L, D)).astype(np.float32)
+    k = bf16(kf)
+    k2 = bf16(torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).float().numpy() * 2)
+    w1 = rng.random((1, Hi)).astype(np.float32)
+    w2 = rng.random((1, Hi)).astype(np.float32)
+    sl = np.array([L], np.int32)
+    s1 = oracle.index_scores(q, w1, k, sl)
+    s2 = oracle.index_scores(q, w2, k, sl)
+    s12 = oracle.index_scores(q, (w1.astype(np.float64) + w2).astype(np.float32), k, sl)
+    np.testing.assert_allclose(s12, s1 + s2, rtol=1e-6)  # w1+w2 rounds to f32
+    np.testing.assert_allclose(oracle.index_scores(q, w1, k2, sl), 2 * s1, rtol=1e-14)
+    assert (oracle.index_scores(bf16(np.zeros((1, Hi, D))), w1, k, sl) == 0).all()
+
+
+def test_scores_row_to_sequence_mapping_and_length_mask():
+    rng = np.random.default_rng(4)
+    S, K, Hi, D, cap = 2, 2, 2, 16, 12
+    k = bf16(rng.standard_normal((S, cap, D)))
+    q = bf16(rng.standard_normal((S * K, Hi, D)))
+    w = rng.random((S * K, Hi)).astype(np.float32)
+    sl = np.array([5, 6, 11, 12], np.int32)
+    sc = oracle.index_scores(q, w, k, sl, rows_per_seq=K, max_len=12)
+    for r in range(S * K):
+        s = r // K
+        alone = oracle.index_scores(q[r:r + 1], w[r:r + 1], k[s:s + 1], sl[r:r + 1], 1, 12)
+        np.testing.assert_array_equal(sc[r], alone[0])
+        assert (sc[r, sl[r]:] == 0).all()
+    # a different sequence's keys give different scores
+    assert not np.array_equal(sc[1, :5], oracle.index_scores(q[1:2], w[1:2], k[1:2], sl[:1], 1, 5)[0])
+
+
+# ---------------------------------------------------------------- select
+
+def brute_force_topk(scores, L, k):
+    """The unique subset whose every member beats every non-member under
+    (score desc, index asc), found by trying all subsets."""
+    n = min(k, L)
+    beats = lambda a, b: scores[a] > scores[b] or (scores[a] == scores[b] and a < b)
+    found = []
+    for sub in itertools.combinations(range(L), n):
+        ss = set(sub)
+        if all(beats(a, b) for a in sub for b in range(L) if b not in ss):
+            found.append(sub)
+    assert len(found) == 1
+    return list(found[0]) + [-1] * (k - n)
+
+
+def test_topk_equals_brute_force_over_all_subsets():
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        L = int(rng.integers(0, 10))
+        k = int(rng.integers(1, 6))
+        sc = rng.integers(-2, 3, size=max(L, 1)).astype(np.float64)  # many ties
+        got = oracle.topk_row(sc, L, k)
+        assert list(got) == brute_force_topk(sc, L, k), (sc, L, k)
+
+
+def test_topk_equals_numpy_lexsort_on_large_rows():
+    rng = np.random.default_rng(6)
+    R, L, k = 3, 5000, 300
+    sc = np.round(rng.standard_normal((R, L)) * 8) / 8  # heavy ties
+    sel = oracle.topk(sc, np.full(R, L, np.int32), k)
+    for r in range(R):
+        order = np.lexsort((np.arange(L), -sc[r]))
+        np.testing.assert_array_equal(sel[r], np.sort(order[:k]))
+        # invariants
+        chosen = set(sel[r].tolist())
+        mn = sc[r, sel[r]].min()
+        for t in range(L):
+            if t not in chosen:
+                assert sc[r, t] < mn or (sc[r, t] == mn and t > max(i for i in chosen if sc[r, i] == mn))
+
+
+def test_topk_ties_signed_zero_short_rows_and_nan():
+    assert list(oracle.topk_row(np.ones(10), 10, 4)) == [0, 1, 2, 3]
+    sc = np.array([0.0, -0.0, 0.0, -0.0, -1.0])
+    assert list(oracle.topk_row(sc, 5, 3)) == [0, 1, 2]
+    sc = np.array([-0.0, 0.0, -1.0])
+    assert list(oracle.topk_row(sc, 3, 1)) == [0]
+    assert list(oracle.topk_row(np.arange(5.0), 5, 8)) == [0, 1, 2, 3, 4, -1, -1, -1]
+    assert list(oracle.topk_row(np.arange(5.0), 0, 3)) == [-1, -1, -1]
+    assert list(oracle.topk_row(np.array([1.0, 5.0, 3.0, 5.0]), 4, 2)) == [1, 3]
+    with pytest.raises(oracle.OracleError):
+        oracle.topk_row(np.array([1.0, np.nan]), 2, 1)
+
+
+# ---------------------------------------------------------------- attend
+
+def dequant(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def bf16_to_f64(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def test_attend_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "attend_worked.json")))
+    q = bf16(np.array(g["q"])[None, None])
+    kv = np.array(g["latent_codes"], np.uint8)[None]  # one page of 2 slots
+    out = oracle.mla_decode(q, kv, np.array([[0]], np.int32), np.array([2], np.int32),
+                            np.array([[0, 1]], np.int32), g["kv_scale"], g["sm_scale"])
+    np.testing.assert_allclose(out[0, 0], g["expected_out"], rtol=1e-15)
+
+
+def small_attend_inputs(seed, L, top_k, H=3, Dl=24, ps=4, S=1, K=1):
+    w = wl.custom(num_seqs=S, rows_per_seq=K, num_heads=H, latent_dim=Dl, index_heads=2,
+                  index_dim=16, top_k=top_k, page_size=ps, seed=seed, context=L)
+    return wl.make_inputs(w)
+
+
+def test_attend_with_every_token_selected_is_dense_attention():
+    for seed, L, ps in [(10, 13, 4), (11, 40, 8), (12, 7, 16)]:
+        x = small_attend_inputs(seed, L, top_k=64, ps=ps)
+        sel = oracle.topk(np.zeros((1, L)), x["seq_lens"], 64)
+        out = oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"], sel,
+                                x["kv_scale"], x["sm_scale"])
+        # dense attention from scratch: gather every token through the table
+        bt = x["block_tables"][0]
+        c = np.stack([dequant(x["kv_cache"][bt[t // ps], t % ps]) for t in range(L)]) * x["kv_scale"]
+        qd = bf16_to_f64(x["q"][0])
+        z = x["sm_scale"] * qd @ c.T
+        p = torch.softmax(torch.from_numpy(z), dim=-1).numpy()
+        np.testing.assert_allclose(out[0], p @ c, rtol=1e-12, atol=1e-14)
+
+
+def test_attend_single_row_identical_rows_and_weights():
+    x = small_attend_inputs(20, L=9, top_k=4)
+    kv, bt, sl = x["kv_cache"], x["block_tables"], x["seq_lens"]
+    one = np.array([[5, -1, -1, -1]], np.int32)
+    sl1 = np.array([6], np.int32)  # top_k 4 > ... use a row of length 1 instead
+    out = oracle.mla_decode(x["q"], kv, bt, np.array([1], np.int32), np.array([[0, -1, -1, -1]], np.int32),
+                            x["kv_scale"], x["sm_scale"])
+    ps = x["page_size"]
+    row0 = dequant(kv[bt[0, 0], 0]) * x["kv_scale"]
+    for h in range(x["num_heads"]):
+        np.testing.assert_array_equal(out[0, h], row0)
+    # identical rows: copy token 0's row onto tokens 1..8
+    kv2 = kv.copy()
+    for t in range(1, 9):
+        kv2[bt[0, t // ps], t % ps] = kv[bt[0, 0], 0]
+    sel = np.array([[0, 3, 5, 8]], np.int32)
+    out2 = oracle.mla_decode(x["q"], kv2, bt, sl, sel, x["kv_scale"], x["sm_scale"])
+    np.testing.assert_allclose(out2[0], np.broadcast_to(row0, out2[0].shape), rtol=1e-14, atol=1e-15)
+    p = oracle.softmax_weights(x["q"], kv, bt, sl, sel, x["kv_scale"], x["sm_scale"], 0, 1)
+    assert abs(p.sum() - 1.0) < 1e-12 and (p > 0).all()
+    del one, sl1
+
+
+def test_attend_invariant_under_page_permutation_and_kv_scale_law():
+    x = small_attend_inputs(30, L=29, top_k=8, ps=4, S=2, K=2)
+    sel = np.array([[0, 3, 7, 9, 12, 20, 27, 28]] * 4, np.int32)
+    sel[0, -1] = 1  # row 0 has length 29 too; keep every id < L
+    base = oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"], sel,
+                             x["kv_scale"], x["sm_scale"], rows_per_seq=2)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(x["num_pages"])
+    kv = np.empty_like(x["kv_cache"])
+    kv[perm] = x["kv_cache"]
+    bt = np.where(x["block_tables"] >= 0, perm[np.maximum(x["block_tables"], 0)], -1).astype(np.int32)
+    moved = oracle.mla_decode(x["q"], kv, bt, x["seq_lens"], sel, x["kv_scale"], x["sm_scale"],
+                              rows_per_seq=2)
+    np.testing.assert_array_equal(base, moved)
+    # doubling kv_scale while halving sm_scale keeps the logits and doubles the output
+    dbl = oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"], sel,
+                            2 * x["kv_scale"], x["sm_scale"] / 2, rows_per_seq=2)
+    np.testing.assert_allclose(dbl, 2 * base, rtol=1e-13, atol=1e-15)
+    # each row reads its own sequence's table (r // K): the batched call equals
+    # one-row calls made with that table alone
+    for r in range(4):
+        alone = oracle.mla_decode(x["q"][r:r + 1], x["kv_cache"], x["block_tables"][r // 2:r // 2 + 1],
+                                  x["seq_lens"][r:r + 1], sel[r:r + 1], x["kv_scale"], x["sm_scale"])
+        np.testing.assert_array_equal(alone[0], base[r])
+    # rows 2,3 read sequence 1's table: swapping the sequences' tables changes them
+    swapped = oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"][::-1].copy(), x["seq_lens"],
+                                sel, x["kv_scale"], x["sm_scale"], rows_per_seq=2)
+    assert not np.allclose(swapped[2:], base[2:])
+
+
+def test_attend_empty_row_is_zero_and_bad_ids_are_refused():
+    x = small_attend_inputs(40, L=9, top_k=4)
+    out = oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"], np.array([0], np.int32),
+                            np.full((1, 4), -1, np.int32), x["kv_scale"], x["sm_scale"])
+    assert (out == 0).all()
+    with pytest.raises(oracle.OracleError):
+        oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"],
+                          np.array([[0, 1, 2, 9]], np.int32), x["kv_scale"], x["sm_scale"])
