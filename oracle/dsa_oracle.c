@@ -261,7 +261,6 @@ int oracle_mla_decode(int R, int K, int H, int Dl,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t rh = 0; rh < (int64_t)R * H; rh++) {
         int r = (int)(rh / H);
-        int h = (int)(rh % H);
         int s = r / K;
         int64_t L = seq_lens[r];
         int64_t n = L < top_k ? L : top_k;

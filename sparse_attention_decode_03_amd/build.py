@@ -1,0 +1,66 @@
+"""Build libdsa.so (the HIP kernels and the C ABI of include/dsa.h) for gfx950.
+
+Every translation unit is compiled with hipcc in parallel, then linked into
+`libdsa.so` next to this file. The packed-fp32 target feature is switched
+off on every hipcc line (the compiler still vectorises fp32 on its own, and
+this keeps it to plain single-lane fp32 instructions).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libdsa.so")
+SOURCES = ["dsa_abi.hip", "index_scores.hip", "topk_select.hip", "mla_decode.hip"]
+ARCH = "gfx950"
+
+COMMON = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the DSA library needs ROCm's hipcc to build")
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libdsa.so (always rebuilds)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,263 @@
+// dsa_abi.hip -- the C ABI of include/dsa.h: host-side validation, workspace
+// carve-up and launch composition. Every refusal happens here, before any HIP
+// call, in the manner of the glm5next_dsa/layer.rs source page (`decode_k`
+// bails out on lockstep, row-count and metadata mismatches before touching the
+// device; `indexer_forward` checks room before any write).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dsa.h"
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptr(const void *p, const char *name)
+{
+    if (!p)
+        return fail(DSA_EINVAL, "%s is NULL", name);
+    if (!aligned16(p))
+        return fail(DSA_EINVAL, "%s is not 16-byte aligned", name);
+    return DSA_OK;
+}
+
+int check_shape(const dsa_shape *sh, dsa::LaunchShape *ls)
+{
+    if (!sh)
+        return fail(DSA_EINVAL, "shape is NULL");
+    if (sh->num_seqs < 1 || sh->rows_per_seq < 1 || sh->num_heads < 1 || sh->latent_dim < 1 ||
+        sh->index_heads < 1 || sh->index_dim < 1 || sh->top_k < 1 || sh->page_size < 1 ||
+        sh->max_len < 1 || sh->k_capacity < 1 || sh->max_blocks_per_seq < 1 || sh->num_pages < 1)
+        return fail(DSA_EINVAL, "every dsa_shape field must be positive");
+    if (sh->rows_per_seq > 8)
+        return fail(DSA_EUNSUPPORTED, "rows_per_seq %d outside [1, 8]", sh->rows_per_seq);
+    if (sh->latent_dim != 512)
+        return fail(DSA_EUNSUPPORTED, "latent_dim %d: only 512 is supported", sh->latent_dim);
+    if (sh->num_heads > 128)
+        return fail(DSA_EUNSUPPORTED, "num_heads %d above 128", sh->num_heads);
+    if (sh->index_heads > 32)
+        return fail(DSA_EUNSUPPORTED, "index_heads %d above 32", sh->index_heads);
+    if (sh->index_dim != 64 && sh->index_dim != 128)
+        return fail(DSA_EUNSUPPORTED, "index_dim %d: only 64 and 128 are supported", sh->index_dim);
+    if (sh->top_k > 16384)
+        return fail(DSA_EUNSUPPORTED, "top_k %d above 16384", sh->top_k);
+    if (sh->max_len > (1 << 22))
+        return fail(DSA_ERANGE, "max_len %d above 4194304", sh->max_len);
+    if (sh->k_capacity < sh->max_len)
+        return fail(DSA_ERANGE, "k_capacity %d below max_len %d", sh->k_capacity, sh->max_len);
+    if ((int64_t)sh->max_blocks_per_seq * sh->page_size < sh->max_len)
+        return fail(DSA_ERANGE,
+                    "block table too short: %d entries x page_size %d cannot address max_len %d",
+                    sh->max_blocks_per_seq, sh->page_size, sh->max_len);
+    const int64_t rows = (int64_t)sh->num_seqs * sh->rows_per_seq;
+    if (rows > 65535)
+        return fail(DSA_EUNSUPPORTED, "%lld rows above 65535", (long long)rows);
+    ls->num_seqs = sh->num_seqs;
+    ls->rows_per_seq = sh->rows_per_seq;
+    ls->num_rows = (int)rows;
+    ls->num_heads = sh->num_heads;
+    ls->latent_dim = sh->latent_dim;
+    ls->index_heads = sh->index_heads;
+    ls->index_dim = sh->index_dim;
+    ls->top_k = sh->top_k;
+    ls->page_size = sh->page_size;
+    ls->max_len = sh->max_len;
+    ls->k_capacity = sh->k_capacity;
+    ls->max_blocks = sh->max_blocks_per_seq;
+    ls->num_pages = sh->num_pages;
+    return DSA_OK;
+}
+
+int check_ws(const void *ws, size_t ws_bytes, const dsa::Workspace &wl)
+{
+    if (check_ptr(ws, "ws") != DSA_OK)
+        return fail(DSA_EWORKSPACE, "workspace is NULL or not 16-byte aligned");
+    if (ws_bytes < wl.total)
+        return fail(DSA_EWORKSPACE, "workspace of %zu bytes is below the %zu this shape needs",
+                    ws_bytes, wl.total);
+    return DSA_OK;
+}
+
+int launched(int rc, const char *what)
+{
+    if (rc != 0)
+        return fail(DSA_ELAUNCH, "HIP refused the %s launch: %s", what,
+                    hipGetErrorString(hipGetLastError()));
+    return DSA_OK;
+}
+
+} // namespace
+
+namespace dsa {
+
+Workspace workspace_layout(const LaunchShape &ls)
+{
+    Workspace w{};
+    const size_t R = (size_t)ls.num_rows;
+    const size_t nc = (size_t)sel_chunks(ls);
+    const size_t nch = (size_t)att_chunks(ls);
+    const size_t hgc = (size_t)att_head_groups(ls);
+    size_t off = 0;
+    w.hist = off;
+    off = align256(off + R * kHistBins * sizeof(uint32_t));
+    w.selrow = off;
+    off = align256(off + R * sizeof(SelRow));
+    w.clear_bytes = off;
+    w.n_gt = off;
+    off = align256(off + R * nc * sizeof(uint32_t));
+    w.offsets = off;
+    off = align256(off + R * nc * sizeof(uint32_t));
+    w.cand = off;
+    off = align256(off + R * (size_t)ls.max_len * 8);
+    w.part_ml = off;
+    w.part_o = off;
+    if (nch > 1) {
+        off = align256(off + R * hgc * nch * kAttHeads * 2 * sizeof(float));
+        w.part_o = off;
+        off = align256(off + R * hgc * nch * kAttHeads * 512 * sizeof(float));
+    }
+    w.total = off;
+    return w;
+}
+
+} // namespace dsa
+
+extern "C" {
+
+size_t dsa_workspace_bytes(const dsa_shape *shape)
+{
+    dsa::LaunchShape ls;
+    if (check_shape(shape, &ls) != DSA_OK)
+        return 0;
+    return dsa::workspace_layout(ls).total;
+}
+
+const char *dsa_last_error(void) { return g_err; }
+
+size_t dsa_bt_entries_needed(size_t seq_len, size_t k, size_t block_size)
+{
+    return (seq_len + k) / (block_size ? block_size : 1) + 2;
+}
+
+int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
+                     const void *k_normed, const int32_t *seq_lens, float *scores, void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if ((rc = check_ptr(q_idx, "q_idx")) || (rc = check_ptr(w, "w")) ||
+        (rc = check_ptr(k_normed, "k_normed")) || (rc = check_ptr(seq_lens, "seq_lens")) ||
+        (rc = check_ptr(scores, "scores")))
+        return rc;
+    return launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
+                                             (const uint16_t *)k_normed, seq_lens, scores,
+                                             nullptr, (hipStream_t)stream),
+                    "index_scores");
+}
+
+int dsa_topk_select(const dsa_shape *shape, const float *scores, const int32_t *seq_lens,
+                    int32_t *sel, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if ((rc = check_ptr(scores, "scores")) || (rc = check_ptr(seq_lens, "seq_lens")) ||
+        (rc = check_ptr(sel, "sel")))
+        return rc;
+    const dsa::Workspace wl = dsa::workspace_layout(ls);
+    if ((rc = check_ws(ws, ws_bytes, wl)) != DSA_OK)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    char *wsb = (char *)ws;
+    if ((rc = launched(dsa::launch_clear(wsb, wl.clear_bytes, st), "clear")) ||
+        (rc = launched(dsa::launch_score_hist(ls, scores, seq_lens, (uint32_t *)(wsb + wl.hist), st),
+                       "score_hist")) ||
+        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, st), "select")))
+        return rc;
+    return DSA_OK;
+}
+
+int dsa_mla_decode(const dsa_shape *shape, const void *q, const uint8_t *kv_cache,
+                   const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
+                   float kv_scale, float sm_scale, void *out, void *ws, size_t ws_bytes,
+                   void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if ((rc = check_ptr(q, "q")) || (rc = check_ptr(kv_cache, "kv_cache")) ||
+        (rc = check_ptr(block_tables, "block_tables")) || (rc = check_ptr(seq_lens, "seq_lens")) ||
+        (rc = check_ptr(sel, "sel")) || (rc = check_ptr(out, "out")))
+        return rc;
+    if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f) || kv_scale == __builtin_huge_valf() ||
+        sm_scale == __builtin_huge_valf())
+        return fail(DSA_EINVAL, "kv_scale and sm_scale must be positive and finite");
+    const dsa::Workspace wl = dsa::workspace_layout(ls);
+    if ((rc = check_ws(ws, ws_bytes, wl)) != DSA_OK)
+        return rc;
+    return launched(dsa::launch_mla_decode(ls, (const uint16_t *)q, kv_cache, block_tables,
+                                           seq_lens, sel, kv_scale, sm_scale, (uint16_t *)out,
+                                           (char *)ws, wl, (hipStream_t)stream),
+                    "mla_decode");
+}
+
+int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, const void *k_normed,
+                 const void *q, const uint8_t *kv_cache, const int32_t *block_tables,
+                 const int32_t *seq_lens, float kv_scale, float sm_scale, float *scores,
+                 int32_t *sel, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if ((rc = check_ptr(q_idx, "q_idx")) || (rc = check_ptr(w, "w")) ||
+        (rc = check_ptr(k_normed, "k_normed")) || (rc = check_ptr(q, "q")) ||
+        (rc = check_ptr(kv_cache, "kv_cache")) || (rc = check_ptr(block_tables, "block_tables")) ||
+        (rc = check_ptr(seq_lens, "seq_lens")) || (rc = check_ptr(scores, "scores")) ||
+        (rc = check_ptr(sel, "sel")) || (rc = check_ptr(out, "out")))
+        return rc;
+    if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f) || kv_scale == __builtin_huge_valf() ||
+        sm_scale == __builtin_huge_valf())
+        return fail(DSA_EINVAL, "kv_scale and sm_scale must be positive and finite");
+    const dsa::Workspace wl = dsa::workspace_layout(ls);
+    if ((rc = check_ws(ws, ws_bytes, wl)) != DSA_OK)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    char *wsb = (char *)ws;
+    if ((rc = launched(dsa::launch_clear(wsb, wl.clear_bytes, st), "clear")) ||
+        (rc = launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
+                                                (const uint16_t *)k_normed, seq_lens, scores,
+                                                (uint32_t *)(wsb + wl.hist), st),
+                       "index_scores")) ||
+        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, st), "select")) ||
+        (rc = launched(dsa::launch_mla_decode(ls, (const uint16_t *)q, kv_cache, block_tables,
+                                              seq_lens, sel, kv_scale, sm_scale, (uint16_t *)out,
+                                              wsb, wl, st),
+                       "mla_decode")))
+        return rc;
+    return DSA_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,110 @@
+// dsa_device.h -- small device-side helpers shared by the gfx950 kernels of
+// the DSA decode path (vector types, matrix-core wrappers, number formats,
+// the order-preserving score key and block-wide scans).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16). Lane l supplies row l%16 of
+// A and column l%16 of B, eight consecutive k each (k block l/16); it receives
+// D[4*(l/16) + v][l%16] in element v.
+__device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16). Lane l supplies row l%32 of
+// A and column l%32 of B (k block l/32); it receives
+// D[8*(v/4) + 4*(l/32) + v%4][l%32] in element v.
+__device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two OCP E4M3 bytes (byte pair HI of `word`) -> two bf16 packed in a dword.
+// Every E4M3 value is exactly representable in bf16, so the conversion through
+// fp32 is exact; the bf16 code is the upper half of the fp32 code.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t word)
+{
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(word, HI);
+    uint32_t lo_bits = __float_as_uint(f.x);
+    uint32_t hi_bits = __float_as_uint(f.y);
+    return (hi_bits & 0xFFFF0000u) | (lo_bits >> 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+// Order-preserving unsigned key of an fp32 score: a > b  <=>  key(a) > key(b)
+// for non-NaN a, b, with -0.0 mapped onto +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive prefix sum of one value per thread (blockDim.x == NT).
+// `scratch` holds NT/64 + 1 words of LDS. Returns the exclusive prefix; the
+// block total lands in *total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
+                                                         uint32_t *total)
+{
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wid = threadIdx.x / kWave;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == kWave - 1)
+        scratch[wid] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        uint32_t s = scratch[w];
+        base += (w < wid) ? s : 0u;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + x - v;
+}
+
+} // namespace dsa

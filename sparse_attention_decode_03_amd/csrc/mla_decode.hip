@@ -1,0 +1,344 @@
+// mla_decode.hip -- FP8 paged NoPE MLA gather-attend on the gfx950 matrix cores.
+//
+// For each row r and head h, over the n_r = min(top_k, L_r) selected tokens
+// (glm5next_dsa/layer.rs source page: module header, fourth trap; doc of
+// `attend_rows`; the `kv_scale` field; `decode_k` for the paged slot):
+//   c_j = kv_scale * e4m3(latent row of token sel[r, j])
+//   z_j = sm_scale * q[r, h, :] . c_j,   out[r, h, :] = sum_j softmax(z)_j c_j
+//
+// Decomposition (a function of the row alone, never of R, so every row is
+// bit-reproducible whichever rows share a launch):
+//  - A row's selection is cut into chunks of 256 slots. One workgroup
+//    (4 waves x 16 heads = 64 heads) handles one chunk: it walks the chunk in
+//    steps of 32 tokens, gathering each token's 512-byte FP8 row through the
+//    block table with coalesced 16-byte loads, dequantising it exactly to
+//    bf16 (E4M3 is a subset of bf16; kv_scale is folded into the logit scale
+//    and the output) and parking the 32 x 512 tile in LDS, token-major, with
+//    an XOR swizzle that keeps both operand reads below free of bank
+//    conflicts.
+//  - QK: S^T[token, head] on 16x16x32 bf16 MFMA, the tile as A (k = latent
+//    dim), Q as B (held in registers for the whole chunk). Tokens are fed to
+//    the MFMA rows in an order that leaves each lane with eight consecutive
+//    tokens of one head -- exactly the k-run the PV operand needs, so the
+//    probabilities never leave registers.
+//  - Online softmax in fp32 (log2 domain, exp2), fixed-order reductions.
+//  - PV: O[head, d] on 16x16x32 bf16 MFMA, P (bf16) as A, the tile as B read
+//    through LDS transpose loads (ds_read_tr16_b64), fp32 accumulators.
+//  - A row with one chunk writes its bf16 output directly. Otherwise every
+//    chunk writes (m, l, O) partials and k_mla_merge folds them in chunk
+//    order 0, 1, 2, ... with the same fp32 formula for every row.
+#include "dsa_device.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+constexpr int kAttThreads = 256;
+constexpr int kStep = 32;          // tokens per LDS tile
+constexpr int kLat = 512;          // latent width
+constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 token row (64)
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// XOR swizzle of a token row's 16-byte chunks. A QK operand read touches 16
+// rows at one chunk index: the swizzle gives them 16 distinct low-four-bit
+// chunk positions, i.e. all 64 banks. A transpose read touches 4 consecutive
+// rows at one chunk pair: the swizzle moves each row to a different pair, so
+// the 16 lanes' 8-byte reads land on 32 distinct banks.
+__device__ __forceinline__ int tok_swz(int t)
+{
+    return 2 * (t & 3) + 8 * ((t >> 3) & 1) + ((t >> 4) & 1);
+}
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
+    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+    const int32_t *__restrict__ bt, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel, float *__restrict__ part_o, float2 *__restrict__ part_ml,
+    uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
+    int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
+{
+    __shared__ u32x4 tile[kStep * kRowChunks]; // 32 KiB, bf16 token-major
+    __shared__ int tok_ok[kStep];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    const int g = lane >> 4;
+    const int n16 = lane & 15;
+    const int r = blockIdx.y;
+    const int c = blockIdx.x % nch_max;
+    const int hg = blockIdx.x / nch_max;
+    const int s = r / K;
+    const int L = min(max(seq_lens[r], 0), max_len);
+    const int n = min(top_k, L);
+    const int nch = (n + kAttChunk - 1) / kAttChunk;
+    const int h_base = hg * kAttHeads + wave * 16;
+
+    if (n == 0) {
+        if (c == 0) {
+            for (int i = tid; i < kAttHeads * kLat; i += kAttThreads) {
+                const int h = hg * kAttHeads + i / kLat;
+                if (h < H)
+                    out[((int64_t)r * H + h) * kLat + (i % kLat)] = 0;
+            }
+        }
+        return;
+    }
+    if (c >= nch)
+        return;
+    const bool wave_active = h_base < H;
+
+    // Q as the B operand of QK: column = head h_base + n16, k = latent dims
+    // 32*ks + 8*g .. +7.
+    bf16x8 qb[16];
+    {
+        const int h = h_base + n16;
+        const uint16_t *qrow = q + ((int64_t)r * H + (h < H ? h : 0)) * kLat;
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (h < H)
+                v = *(const u32x4 *)(qrow + 32 * ks + 8 * g);
+            qb[ks] = as_bf16x8(v);
+        }
+    }
+
+    float m_run = kNegInf; // running max of the log2-domain logits (head n16)
+    float l_run = 0.0f;    // running sum of exp2(z - m_run)
+    floatx4 o[32];
+#pragma unroll
+    for (int nt = 0; nt < 32; nt++)
+        o[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int tq = tid >> 5; // staging: tokens 4*tq .. 4*tq+3
+    const int dc = tid & 31; //          latent bytes 16*dc .. 16*dc+15
+    const int slot_end = min(n, (c + 1) * kAttChunk);
+    const int32_t *srow = sel + (int64_t)r * top_k;
+    const int32_t *btrow = bt + (int64_t)s * max_blocks;
+
+    // Gather of one step's 32 FP8 rows into registers (issued one step ahead).
+    u32x4 raw[4];
+    bool ok[4];
+    auto gather = [&](int base) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int slot = base + 4 * tq + i;
+            int t = slot < slot_end ? srow[slot] : -1;
+            bool v = t >= 0 && t < L;
+            int page = v ? btrow[t / ps] : -1;
+            v = v && page >= 0 && page < num_pages;
+            ok[i] = v;
+            raw[i] = u32x4{0u, 0u, 0u, 0u};
+            if (v)
+                raw[i] = *(const u32x4 *)(kv + ((int64_t)page * ps + t % ps) * kLat + 16 * dc);
+        }
+    };
+    gather(c * kAttChunk);
+
+    for (int base = c * kAttChunk; base < slot_end; base += kStep) {
+        // ---- dequantise the gathered rows to bf16 and park them in LDS ----
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = 4 * tq + i;
+            u32x4 lo, hi;
+            lo.x = e4m3x2_to_bf16x2<false>(raw[i].x);
+            lo.y = e4m3x2_to_bf16x2<true>(raw[i].x);
+            lo.z = e4m3x2_to_bf16x2<false>(raw[i].y);
+            lo.w = e4m3x2_to_bf16x2<true>(raw[i].y);
+            hi.x = e4m3x2_to_bf16x2<false>(raw[i].z);
+            hi.y = e4m3x2_to_bf16x2<true>(raw[i].z);
+            hi.z = e4m3x2_to_bf16x2<false>(raw[i].w);
+            hi.w = e4m3x2_to_bf16x2<true>(raw[i].w);
+            const int sw = tok_swz(t);
+            tile[t * kRowChunks + ((2 * dc) ^ sw)] = lo;
+            tile[t * kRowChunks + ((2 * dc + 1) ^ sw)] = hi;
+            if (dc == 0)
+                tok_ok[t] = ok[i];
+        }
+        __syncthreads();
+        // ---- next step's rows travel while this step computes ----
+        if (base + kStep < slot_end)
+            gather(base + kStep);
+
+        if (wave_active) {
+            // ---- QK: lane ends with head n16, tokens 8g + 4a + v ----
+            floatx4 sacc[2];
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                const int trow = 8 * (n16 >> 2) + 4 * a + (n16 & 3);
+                const int sw = tok_swz(trow);
+                floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < 16; ks++)
+                    acc = mfma16x16x32(as_bf16x8(tile[trow * kRowChunks + ((4 * ks + g) ^ sw)]),
+                                       qb[ks], acc);
+                sacc[a] = acc;
+            }
+            // ---- online softmax (log2 domain) ----
+            float z[8];
+            float mx = kNegInf;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float v = sacc[j >> 2][j & 3] * qk_log2;
+                z[j] = tok_ok[8 * g + j] ? v : kNegInf;
+                mx = __builtin_fmaxf(mx, z[j]);
+            }
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            const float m_new = __builtin_fmaxf(m_run, mx);
+            const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+            const float alpha = exp2f(m_run - m_use);
+            float p[8];
+            float rs = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                p[j] = exp2f(z[j] - m_use);
+                rs += p[j];
+            }
+            rs += __shfl_xor(rs, 16, kWave);
+            rs += __shfl_xor(rs, 32, kWave);
+            l_run = __builtin_fmaf(l_run, alpha, rs);
+            m_run = m_new;
+            u32x4 pw;
+            pw.x = pack_bf16x2(p[0], p[1]);
+            pw.y = pack_bf16x2(p[2], p[3]);
+            pw.z = pack_bf16x2(p[4], p[5]);
+            pw.w = pack_bf16x2(p[6], p[7]);
+            const bf16x8 pa = as_bf16x8(pw);
+            // rescale O rows (heads 4g + v) by their own alpha
+            float av[4];
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                av[v] = __shfl(alpha, 4 * g + v, kWave);
+#pragma unroll
+            for (int nt = 0; nt < 32; nt++) {
+                o[nt][0] *= av[0];
+                o[nt][1] *= av[1];
+                o[nt][2] *= av[2];
+                o[nt][3] *= av[3];
+            }
+            // ---- PV: B = tile^T through transpose loads ----
+            const int tr_row0 = 8 * g + (n16 >> 2);       // tokens 8g + 0..3
+            const int tr_row1 = tr_row0 + 4;              // tokens 8g + 4..7
+            const int sw0 = tok_swz(tr_row0);
+            const int sw1 = tok_swz(tr_row1);
+            const int half = (n16 & 1) * 4;               // shorts within the chunk
+#pragma unroll
+            for (int nt = 0; nt < 32; nt++) {
+                const int ch = 2 * nt + ((n16 & 3) >> 1);
+                const short *p0 = (const short *)&tile[tr_row0 * kRowChunks + (ch ^ sw0)] + half;
+                const short *p1 = (const short *)&tile[tr_row1 * kRowChunks + (ch ^ sw1)] + half;
+                const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p0);
+                const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p1);
+                typedef short shortx8 __attribute__((ext_vector_type(8)));
+                const shortx8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                o[nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, bb), o[nt]);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (!wave_active)
+        return;
+    if (nch == 1) {
+        float inv[4];
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const float lh = __shfl(l_run, 4 * g + v, kWave);
+            inv[v] = lh > 0.0f ? kv_scale / lh : 0.0f;
+        }
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const int h = h_base + 4 * g + v;
+            if (h < H) {
+                uint16_t *orow = out + ((int64_t)r * H + h) * kLat;
+#pragma unroll
+                for (int nt = 0; nt < 32; nt++)
+                    orow[16 * nt + n16] = f32_to_bf16_rne(o[nt][v] * inv[v]);
+            }
+        }
+    } else {
+        const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
+        if (g == 0)
+            part_ml[pbase + wave * 16 + n16] = float2{m_run, l_run};
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            float *prow = part_o + (pbase + wave * 16 + 4 * g + v) * kLat;
+#pragma unroll
+            for (int nt = 0; nt < 32; nt++)
+                prow[16 * nt + n16] = o[nt][v];
+        }
+    }
+}
+
+// Fold the per-chunk partials of every (row, head) in chunk order.
+__global__ __launch_bounds__(128) void k_mla_merge(const float *__restrict__ part_o,
+                                                   const float2 *__restrict__ part_ml,
+                                                   const int32_t *__restrict__ seq_lens,
+                                                   uint16_t *__restrict__ out, int H, int top_k,
+                                                   int max_len, int nch_max, int hg_count,
+                                                   float kv_scale)
+{
+    const int r = blockIdx.y;
+    const int h = blockIdx.x;
+    const int L = min(max(seq_lens[r], 0), max_len);
+    const int n = min(top_k, L);
+    const int nch = (n + kAttChunk - 1) / kAttChunk;
+    if (nch <= 1)
+        return;
+    const int hg = h / kAttHeads;
+    const int hl = h % kAttHeads;
+    const int d = threadIdx.x * 4;
+    float m_acc = kNegInf, l_acc = 0.0f;
+    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < nch; c++) {
+        const int64_t pi = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads + hl;
+        const float2 ml = part_ml[pi];
+        const floatx4 ov = *(const floatx4 *)(part_o + pi * kLat + d);
+        const float m_new = __builtin_fmaxf(m_acc, ml.x);
+        if (m_new == kNegInf)
+            continue;
+        const float a = exp2f(m_acc - m_new);
+        const float b = exp2f(ml.x - m_new);
+        l_acc = __builtin_fmaf(ml.y, b, l_acc * a);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            acc[i] = __builtin_fmaf(ov[i], b, acc[i] * a);
+        m_acc = m_new;
+    }
+    const float inv = l_acc > 0.0f ? kv_scale / l_acc : 0.0f;
+    uint16_t *orow = out + ((int64_t)r * H + h) * kLat + d;
+    u32x2 packed;
+    packed.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    packed.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(u32x2 *)orow = packed;
+}
+
+int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
+                      float kv_scale, float sm_scale, uint16_t *out, char *ws,
+                      const Workspace &wl, hipStream_t stream)
+{
+    const int nch_max = att_chunks(ls) > 0 ? att_chunks(ls) : 1;
+    const int hgc = att_head_groups(ls);
+    const float qk_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634074);
+    float *part_o = (float *)(ws + wl.part_o);
+    float2 *part_ml = (float2 *)(ws + wl.part_ml);
+    hipLaunchKernelGGL(k_mla_decode, dim3(nch_max * hgc, ls.num_rows), dim3(kAttThreads), 0,
+                       stream, q, kv_cache, block_tables, seq_lens, sel, part_o, part_ml, out,
+                       ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size, ls.max_blocks,
+                       ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max, hgc);
+    if (hipGetLastError() != hipSuccess)
+        return -1;
+    if (nch_max > 1) {
+        hipLaunchKernelGGL(k_mla_merge, dim3(ls.num_heads, ls.num_rows), dim3(128), 0, stream,
+                           part_o, part_ml, seq_lens, out, ls.num_heads, ls.top_k, ls.max_len,
+                           nch_max, hgc, kv_scale);
+        if (hipGetLastError() != hipSuccess)
+            return -1;
+    }
+    return 0;
+}
+
+} // namespace dsa
