@@ -64,6 +64,8 @@ int check_shape(const dsa_shape *sh, dsa::LaunchShape *ls)
         return fail(DSA_ERANGE,
                     "block table too short: %d entries x page_size %d cannot address max_len %d",
                     sh->max_blocks_per_seq, sh->page_size, sh->max_len);
+    if ((int64_t)sh->num_pages * sh->page_size > 0x7FFFFFFF)
+        return fail(DSA_ERANGE, "num_pages x page_size above 2^31 - 1 latent rows");
     const int64_t rows = (int64_t)sh->num_seqs * sh->rows_per_seq;
     if (rows > 65535)
         return fail(DSA_EUNSUPPORTED, "%lld rows above 65535", (long long)rows);
@@ -119,6 +121,8 @@ Workspace workspace_layout(const LaunchShape &ls)
     off = align256(off + R * sizeof(SelRow));
     w.clear_bytes = off;
     w.n_gt = off;
+    off = align256(off + R * nc * sizeof(uint32_t));
+    w.n_cand = off;
     off = align256(off + R * nc * sizeof(uint32_t));
     w.offsets = off;
     off = align256(off + R * nc * sizeof(uint32_t));

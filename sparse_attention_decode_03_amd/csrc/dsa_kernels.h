@@ -38,16 +38,15 @@ inline int att_head_groups(const LaunchShape &ls) { return (ls.num_heads + kAttH
 // Per-row selection state in the workspace.
 struct SelRow {
     uint32_t ticket;     // chunk workgroups of this row that have finished
-    uint32_t cand_count; // candidates appended so far
     uint32_t thr_key;    // exact threshold key
     int32_t idx_cut;     // largest selected index among keys equal to thr_key
-    uint32_t pad[4];
+    uint32_t pad[5];
 };
 
 // Workspace carve-up (byte offsets, 256-aligned).
 struct Workspace {
     size_t hist, selrow, clear_bytes; // [0, clear_bytes) is zeroed per call
-    size_t n_gt, offsets, cand;
+    size_t n_gt, n_cand, offsets, cand;
     size_t part_o, part_ml;
     size_t total;
 };

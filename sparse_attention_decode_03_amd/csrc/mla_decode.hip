@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
     __shared__ u32x4 tile[kStep * kRowChunks]; // 32 KiB, bf16 token-major
-    __shared__ int tok_ok[kStep];
+    __shared__ int rowidx[kAttChunk];          // latent row of each slot, -1 = skip
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -88,6 +88,23 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     if (c >= nch)
         return;
     const bool wave_active = h_base < H;
+    const int slot0 = c * kAttChunk;
+    const int slot_end = min(n, slot0 + kAttChunk);
+
+    // ---- resolve the chunk's selected tokens to latent rows once ----
+    {
+        const int slot = slot0 + tid;
+        int row = -1;
+        if (slot < slot_end) {
+            const int t = sel[(int64_t)r * top_k + slot];
+            if (t >= 0 && t < L) {
+                const int page = bt[(int64_t)s * max_blocks + t / ps];
+                if (page >= 0 && page < num_pages)
+                    row = page * ps + t % ps;
+            }
+        }
+        rowidx[tid] = row;
+    }
 
     // Q as the B operand of QK: column = head h_base + n16, k = latent dims
     // 32*ks + 8*g .. +7.
@@ -103,6 +120,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
             qb[ks] = as_bf16x8(v);
         }
     }
+    __syncthreads();
 
     float m_run = kNegInf; // running max of the log2-domain logits (head n16)
     float l_run = 0.0f;    // running sum of exp2(z - m_run)
@@ -113,31 +131,20 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 
     const int tq = tid >> 5; // staging: tokens 4*tq .. 4*tq+3
     const int dc = tid & 31; //          latent bytes 16*dc .. 16*dc+15
-    const int slot_end = min(n, (c + 1) * kAttChunk);
-    const int32_t *srow = sel + (int64_t)r * top_k;
-    const int32_t *btrow = bt + (int64_t)s * max_blocks;
 
-    // Gather of one step's 32 FP8 rows into registers (issued one step ahead).
-    u32x4 raw[4];
-    bool ok[4];
-    auto gather = [&](int base) {
+    // One step's 32 FP8 rows into registers; two steps stay in flight.
+    auto gather = [&](u32x4 (&raw)[4], int base) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int slot = base + 4 * tq + i;
-            int t = slot < slot_end ? srow[slot] : -1;
-            bool v = t >= 0 && t < L;
-            int page = v ? btrow[t / ps] : -1;
-            v = v && page >= 0 && page < num_pages;
-            ok[i] = v;
+            const int k = base - slot0 + 4 * tq + i;
+            const int row = (k < kAttChunk) ? rowidx[k] : -1;
             raw[i] = u32x4{0u, 0u, 0u, 0u};
-            if (v)
-                raw[i] = *(const u32x4 *)(kv + ((int64_t)page * ps + t % ps) * kLat + 16 * dc);
+            if (row >= 0)
+                raw[i] = *(const u32x4 *)(kv + (int64_t)row * kLat + 16 * dc);
         }
     };
-    gather(c * kAttChunk);
-
-    for (int base = c * kAttChunk; base < slot_end; base += kStep) {
-        // ---- dequantise the gathered rows to bf16 and park them in LDS ----
+    // Dequantise (exact) into the bf16 LDS tile.
+    auto stage = [&](const u32x4 (&raw)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * tq + i;
@@ -153,60 +160,53 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
             const int sw = tok_swz(t);
             tile[t * kRowChunks + ((2 * dc) ^ sw)] = lo;
             tile[t * kRowChunks + ((2 * dc + 1) ^ sw)] = hi;
-            if (dc == 0)
-                tok_ok[t] = ok[i];
         }
-        __syncthreads();
-        // ---- next step's rows travel while this step computes ----
-        if (base + kStep < slot_end)
-            gather(base + kStep);
-
-        if (wave_active) {
-            // ---- QK: lane ends with head n16, tokens 8g + 4a + v ----
-            floatx4 sacc[2];
+    };
+    // QK, online softmax and PV over the staged tile of step `base`.
+    auto compute = [&](int base) {
+        // ---- QK: lane ends with head n16, tokens 8g + 4a + v ----
+        floatx4 sacc[2];
 #pragma unroll
-            for (int a = 0; a < 2; a++) {
-                const int trow = 8 * (n16 >> 2) + 4 * a + (n16 & 3);
-                const int sw = tok_swz(trow);
-                floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int a = 0; a < 2; a++) {
+            const int trow = 8 * (n16 >> 2) + 4 * a + (n16 & 3);
+            const int sw = tok_swz(trow);
+            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ks = 0; ks < 16; ks++)
-                    acc = mfma16x16x32(as_bf16x8(tile[trow * kRowChunks + ((4 * ks + g) ^ sw)]),
-                                       qb[ks], acc);
-                sacc[a] = acc;
-            }
-            // ---- online softmax (log2 domain) ----
-            float z[8];
-            float mx = kNegInf;
+            for (int ks = 0; ks < 16; ks++)
+                acc = mfma16x16x32(as_bf16x8(tile[trow * kRowChunks + ((4 * ks + g) ^ sw)]),
+                                   qb[ks], acc);
+            sacc[a] = acc;
+        }
+        // ---- online softmax (log2 domain) ----
+        float z[8];
+        float mx = kNegInf;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float v = sacc[j >> 2][j & 3] * qk_log2;
-                z[j] = tok_ok[8 * g + j] ? v : kNegInf;
-                mx = __builtin_fmaxf(mx, z[j]);
-            }
-            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = __builtin_fmaxf(m_run, mx);
-            const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-            const float alpha = exp2f(m_run - m_use);
-            float p[8];
-            float rs = 0.0f;
+        for (int j = 0; j < 8; j++) {
+            const float v = sacc[j >> 2][j & 3] * qk_log2;
+            z[j] = rowidx[base - slot0 + 8 * g + j] >= 0 ? v : kNegInf;
+            mx = __builtin_fmaxf(mx, z[j]);
+        }
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float m_new = __builtin_fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        float p[8];
+        float rs = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                p[j] = exp2f(z[j] - m_use);
-                rs += p[j];
-            }
-            rs += __shfl_xor(rs, 16, kWave);
-            rs += __shfl_xor(rs, 32, kWave);
-            l_run = __builtin_fmaf(l_run, alpha, rs);
-            m_run = m_new;
-            u32x4 pw;
-            pw.x = pack_bf16x2(p[0], p[1]);
-            pw.y = pack_bf16x2(p[2], p[3]);
-            pw.z = pack_bf16x2(p[4], p[5]);
-            pw.w = pack_bf16x2(p[6], p[7]);
-            const bf16x8 pa = as_bf16x8(pw);
-            // rescale O rows (heads 4g + v) by their own alpha
+        for (int j = 0; j < 8; j++) {
+            p[j] = exp2f(z[j] - m_use);
+            rs += p[j];
+        }
+        rs += __shfl_xor(rs, 16, kWave);
+        rs += __shfl_xor(rs, 32, kWave);
+        l_run = __builtin_fmaf(l_run, alpha, rs);
+        // O rows are heads 4g + v: rescale them by their own alpha, but only
+        // when some head's maximum grew (otherwise every alpha is exactly 1,
+        // or O is still zero, and the multiply would change nothing)
+        const bool grew = __ballot(m_new > m_run && m_run != kNegInf) != 0;
+        m_run = m_new;
+        if (grew) {
             float av[4];
 #pragma unroll
             for (int v = 0; v < 4; v++)
@@ -218,24 +218,52 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 o[nt][2] *= av[2];
                 o[nt][3] *= av[3];
             }
-            // ---- PV: B = tile^T through transpose loads ----
-            const int tr_row0 = 8 * g + (n16 >> 2);       // tokens 8g + 0..3
-            const int tr_row1 = tr_row0 + 4;              // tokens 8g + 4..7
-            const int sw0 = tok_swz(tr_row0);
-            const int sw1 = tok_swz(tr_row1);
-            const int half = (n16 & 1) * 4;               // shorts within the chunk
-#pragma unroll
-            for (int nt = 0; nt < 32; nt++) {
-                const int ch = 2 * nt + ((n16 & 3) >> 1);
-                const short *p0 = (const short *)&tile[tr_row0 * kRowChunks + (ch ^ sw0)] + half;
-                const short *p1 = (const short *)&tile[tr_row1 * kRowChunks + (ch ^ sw1)] + half;
-                const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p0);
-                const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p1);
-                typedef short shortx8 __attribute__((ext_vector_type(8)));
-                const shortx8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                o[nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, bb), o[nt]);
-            }
         }
+        u32x4 pw;
+        pw.x = pack_bf16x2(p[0], p[1]);
+        pw.y = pack_bf16x2(p[2], p[3]);
+        pw.z = pack_bf16x2(p[4], p[5]);
+        pw.w = pack_bf16x2(p[6], p[7]);
+        const bf16x8 pa = as_bf16x8(pw);
+        // ---- PV: B = tile^T through transpose loads ----
+        const int tr_row0 = 8 * g + (n16 >> 2); // tokens 8g + 0..3
+        const int tr_row1 = tr_row0 + 4;        // tokens 8g + 4..7
+        const int sw0 = tok_swz(tr_row0);
+        const int sw1 = tok_swz(tr_row1);
+        const int half = (n16 & 1) * 4; // shorts within the chunk
+#pragma unroll
+        for (int nt = 0; nt < 32; nt++) {
+            const int ch = 2 * nt + ((n16 & 3) >> 1);
+            const short *p0 = (const short *)&tile[tr_row0 * kRowChunks + (ch ^ sw0)] + half;
+            const short *p1 = (const short *)&tile[tr_row1 * kRowChunks + (ch ^ sw1)] + half;
+            const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p0);
+            const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p1);
+            typedef short shortx8 __attribute__((ext_vector_type(8)));
+            const shortx8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            o[nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, bb), o[nt]);
+        }
+    };
+
+    u32x4 ra[4], rb[4];
+    gather(ra, slot0);
+    if (slot0 + kStep < slot_end)
+        gather(rb, slot0 + kStep);
+    for (int base = slot0; base < slot_end; base += 2 * kStep) {
+        stage(ra);
+        __syncthreads();
+        if (base + 2 * kStep < slot_end)
+            gather(ra, base + 2 * kStep);
+        if (wave_active)
+            compute(base);
+        __syncthreads();
+        if (base + kStep >= slot_end)
+            break;
+        stage(rb);
+        __syncthreads();
+        if (base + 3 * kStep < slot_end)
+            gather(rb, base + 3 * kStep);
+        if (wave_active)
+            compute(base + kStep);
         __syncthreads();
     }
 

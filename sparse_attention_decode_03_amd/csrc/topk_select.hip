@@ -11,9 +11,8 @@
 //     scoring pass by dsa_decode_k; a separate pass for dsa_topk_select).
 //  2. k_select_candidates, one workgroup per 4096-token chunk of a row: every
 //     workgroup finds the bin b* that holds the k-th largest key, counts the
-//     keys above b* in its chunk and appends the keys inside b* to a
-//     candidate list (integer atomics only: the list's order varies, but
-//     nothing downstream depends on it). The last workgroup of the row (an
+//     keys above b* in its chunk and compacts the keys inside b* into the
+//     chunk's own candidate region. The last workgroup of the row (an
 //     atomic ticket; no workgroup ever waits) resolves the exact threshold
 //     key T and the index cut among keys equal to T with four more radix
 //     passes over the candidates, then turns per-chunk selected counts into
@@ -131,18 +130,19 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
 __global__ __launch_bounds__(kSelThreads) void k_select_candidates(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
     const uint32_t *__restrict__ hist, SelRow *__restrict__ rows, uint32_t *__restrict__ n_gt,
-    uint32_t *__restrict__ offsets, u32x2 *__restrict__ cand, int max_len, int top_k, int nc_max)
+    uint32_t *__restrict__ n_cand, uint32_t *__restrict__ offsets, u32x2 *__restrict__ cand,
+    int max_len, int top_k, int nc_max)
 {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t chunk_cnt[1024];
+    __shared__ uint32_t chunk_cand[1024];
     __shared__ BinSearch bs;
-    __shared__ uint32_t wave_sum[kSelThreads / kWave];
+    __shared__ uint32_t scan[kSelThreads / kWave + 1];
     __shared__ int is_last;
 
     const int r = blockIdx.y;
     const int c = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid % kWave;
     const int L = min(max(seq_lens[r], 0), max_len);
     if (L <= top_k)
         return;
@@ -159,47 +159,37 @@ __global__ __launch_bounds__(kSelThreads) void k_select_candidates(
     const uint32_t bstar = find_bin<true>(h, kHistBins, (uint32_t)top_k, &bs, &above);
     const uint32_t need = (uint32_t)top_k - above; // keys to take from bin b*
 
-    // ---- this chunk: count keys above b*, append keys inside b* ----
+    // ---- this chunk: count keys above b*, gather keys inside b* into the
+    //      chunk's own candidate region (no cross-workgroup atomics) ----
     const float *row = scores + (int64_t)r * max_len;
     u32x2 *rc = cand + (int64_t)r * max_len;
-    uint32_t gt = 0;
+    uint32_t keys[kSelPerThread];
+    uint32_t inmask = 0, gt = 0, nin = 0;
+#pragma unroll
     for (int i = 0; i < kSelPerThread; i++) {
         const int t = c * kSelChunk + i * kSelThreads + tid;
-        uint32_t key = 0;
-        bool in = false;
+        keys[i] = 0;
         if (t < L) {
-            key = score_key(row[t]);
-            const uint32_t b = key >> kHistShift;
+            keys[i] = score_key(row[t]);
+            const uint32_t b = keys[i] >> kHistShift;
             gt += b > bstar;
-            in = b == bstar;
-        }
-        const uint64_t mask = __ballot(in);
-        if (mask) {
-            const uint32_t n = (uint32_t)__popcll(mask);
-            const int leader = __ffsll((unsigned long long)mask) - 1;
-            uint32_t pos = 0;
-            if (lane == leader)
-                pos = atomicAdd(&st->cand_count, n);
-            pos = __shfl(pos, leader, kWave);
-            if (in) {
-                const uint64_t below = mask & ((1ull << lane) - 1ull);
-                const uint32_t at = pos + (uint32_t)__popcll(below);
-                if (at < (uint32_t)L) // always true for a histogram of these scores
-                    rc[at] = u32x2{key, (uint32_t)t};
+            if (b == bstar) {
+                inmask |= 1u << i;
+                nin++;
             }
         }
     }
-    // block sum of gt
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        gt += __shfl_xor(gt, o, kWave);
-    if (lane == 0)
-        wave_sum[tid / kWave] = gt;
-    __syncthreads();
+    uint32_t n_in_chunk;
+    uint32_t at = block_exclusive_scan<kSelThreads>(nin, scan, &n_in_chunk);
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; i++)
+        if (inmask & (1u << i))
+            rc[c * kSelChunk + at++] = u32x2{keys[i], (uint32_t)(c * kSelChunk + i * kSelThreads + tid)};
+    uint32_t n_gt_chunk;
+    block_exclusive_scan<kSelThreads>(gt, scan, &n_gt_chunk);
     if (tid == 0) {
-        uint32_t tot = 0;
-        for (int i = 0; i < kSelThreads / kWave; i++)
-            tot += wave_sum[i];
-        n_gt[(int64_t)r * nc_max + c] = tot;
+        n_gt[(int64_t)r * nc_max + c] = n_gt_chunk;
+        n_cand[(int64_t)r * nc_max + c] = n_in_chunk;
     }
 
     // ---- the last workgroup of the row resolves the threshold ----
@@ -211,16 +201,28 @@ __global__ __launch_bounds__(kSelThreads) void k_select_candidates(
     if (!is_last)
         return;
     __threadfence();
-    const uint32_t m = min(__hip_atomic_load(&st->cand_count, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT),
-                           (uint32_t)L);
+    for (int i = tid; i < nc; i += kSelThreads) {
+        chunk_cand[i] = min(__hip_atomic_load(&n_cand[(int64_t)r * nc_max + i], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT),
+                            (uint32_t)kSelChunk);
+        chunk_cnt[i] = __hip_atomic_load(&n_gt[(int64_t)r * nc_max + i], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    // visit every candidate of the row (chunk regions, in any order)
+    auto for_each = [&](auto &&f) {
+        for (int cc = 0; cc < nc; cc++) {
+            const uint32_t n = chunk_cand[cc];
+            for (uint32_t i = tid; i < n; i += kSelThreads)
+                f(rc[cc * kSelChunk + i]);
+        }
+    };
 
     // pass A: key bits [20:10] of the candidates, descending
     for (int i = tid; i < kHistBins; i += kSelThreads)
         h[i] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < m; i += kSelThreads)
-        atomicAdd(&h[(rc[i].x >> 10) & 0x7FFu], 1u);
+    for_each([&](u32x2 e) { atomicAdd(&h[(e.x >> 10) & 0x7FFu], 1u); });
     __syncthreads();
     uint32_t bef;
     const uint32_t a_bin = find_bin<true>(h, 2048, need, &bs, &bef);
@@ -231,11 +233,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_candidates(
     for (int i = tid; i < kHistBins; i += kSelThreads)
         h[i] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < m; i += kSelThreads) {
-        const uint32_t k = rc[i].x;
-        if ((k >> 10) == hi21)
-            atomicAdd(&h[k & 0x3FFu], 1u);
-    }
+    for_each([&](u32x2 e) {
+        if ((e.x >> 10) == hi21)
+            atomicAdd(&h[e.x & 0x3FFu], 1u);
+    });
     __syncthreads();
     const uint32_t b_bin = find_bin<true>(h, 1024, need_a, &bs, &bef);
     const uint32_t need_t = need_a - bef; // keys equal to T to take
@@ -249,11 +250,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_candidates(
         for (int i = tid; i < kHistBins; i += kSelThreads)
             h[i] = 0u;
         __syncthreads();
-        for (uint32_t i = tid; i < m; i += kSelThreads) {
-            const u32x2 e = rc[i];
+        for_each([&](u32x2 e) {
             if (e.x == T)
                 atomicAdd(&h[(e.y >> 11) & 0x7FFu], 1u);
-        }
+        });
         __syncthreads();
         const uint32_t c_bin = find_bin<false>(h, 2048, need_t, &bs, &bef);
         const uint32_t need_c = need_t - bef;
@@ -261,25 +261,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select_candidates(
         for (int i = tid; i < kHistBins; i += kSelThreads)
             h[i] = 0u;
         __syncthreads();
-        for (uint32_t i = tid; i < m; i += kSelThreads) {
-            const u32x2 e = rc[i];
+        for_each([&](u32x2 e) {
             if (e.x == T && (e.y >> 11) == c_bin)
                 atomicAdd(&h[e.y & 0x7FFu], 1u);
-        }
+        });
         __syncthreads();
         const uint32_t d_bin = find_bin<false>(h, 2048, need_c, &bs, &bef);
         cut = (int32_t)((c_bin << 11) | d_bin);
     }
 
     // per-chunk selected counts -> exclusive offsets
-    for (int i = tid; i < nc; i += kSelThreads)
-        chunk_cnt[i] = n_gt[(int64_t)r * nc_max + i];
-    __syncthreads();
-    for (uint32_t i = tid; i < m; i += kSelThreads) {
-        const u32x2 e = rc[i];
+    for_each([&](u32x2 e) {
         if (e.x > T || (e.x == T && (int32_t)e.y <= cut))
             atomicAdd(&chunk_cnt[e.y / kSelChunk], 1u);
-    }
+    });
     __syncthreads();
     if (tid == 0) {
         uint32_t run = 0;
@@ -349,10 +344,12 @@ int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq
     const uint32_t *hist = (const uint32_t *)(ws + wl.hist);
     SelRow *rows = (SelRow *)(ws + wl.selrow);
     uint32_t *n_gt = (uint32_t *)(ws + wl.n_gt);
+    uint32_t *n_cand = (uint32_t *)(ws + wl.n_cand);
     uint32_t *offs = (uint32_t *)(ws + wl.offsets);
     u32x2 *cand = (u32x2 *)(ws + wl.cand);
     hipLaunchKernelGGL(k_select_candidates, dim3(nc, ls.num_rows), dim3(kSelThreads), 0, stream,
-                       scores, seq_lens, hist, rows, n_gt, offs, cand, ls.max_len, ls.top_k, nc);
+                       scores, seq_lens, hist, rows, n_gt, n_cand, offs, cand, ls.max_len,
+                       ls.top_k, nc);
     if (hipGetLastError() != hipSuccess)
         return -1;
     const int ncc = (ls.max_len > ls.top_k ? ls.max_len : ls.top_k);
