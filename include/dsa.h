@@ -85,9 +85,10 @@ typedef struct dsa_shape {
 
 /*
  * Bytes of caller-owned device workspace that dsa_topk_select, dsa_mla_decode
- * and dsa_decode_k need for `shape` (selection histograms, candidates and
- * per-chunk attention partials). Its contents need no initialisation: every
- * call clears what it uses. Calls that share one workspace must not overlap.
+ * and dsa_decode_k need for `shape` (selection candidates and bitmaps past
+ * their on-chip capacity, per-chunk attention partials). Its contents need no initialisation: every
+ * call writes each part before reading it. Calls that share one workspace
+ * must not overlap.
  * Returns 0 for a shape that dsa_decode_k would refuse.
  */
 size_t dsa_workspace_bytes(const dsa_shape *shape);
@@ -106,7 +107,9 @@ size_t dsa_workspace_bytes(const dsa_shape *shape);
  *   w        [R, Hi]    fp32
  *   k_normed [S, k_capacity, D] bf16, token-major (D * 2 bytes per token)
  *   seq_lens [R] int32
- *   scores   [R, max_len] fp32 (output; entries t >= L_r are not written)
+ *   scores   [R, dsa_score_stride(shape)] fp32 (output; the row stride is
+ *            max_len rounded up to a multiple of 64, so rows are 256-byte
+ *            aligned; entries t >= L_r are not written)
  */
 int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
                      const void *k_normed, const int32_t *seq_lens, float *scores,
@@ -119,8 +122,9 @@ int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
  * order with a unique top-k prefix). Read per token: row r selects the
  * n_r = min(top_k, L_r) tokens of [0, L_r) that come first under (score
  * descending, index ascending), with -0.0 equal to +0.0.
- *   scores   [R, max_len] fp32 (only [0, L_r) of each row is read; NaN scores
- *            are ordered by their bit pattern and are out of contract)
+ *   scores   [R, dsa_score_stride(shape)] fp32 (only [0, L_r) of each row is
+ *            read; NaN scores are ordered by their bit pattern and are out of
+ *            contract)
  *   seq_lens [R] int32
  *   sel      [R, top_k] int32 (output): the n_r selected ids in ascending
  *            order, then -1 in every slot past n_r
@@ -174,6 +178,12 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w,
                  const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
                  float sm_scale, float *scores, int32_t *sel, void *out, void *ws,
                  size_t ws_bytes, void *stream);
+
+/*
+ * Row stride, in floats, of every scores buffer for `shape`: max_len rounded
+ * up to a multiple of 64. Returns 0 for a shape the entry points refuse.
+ */
+size_t dsa_score_stride(const dsa_shape *shape);
 
 /*
  * Block-table entries a paged gather can touch for k query rows starting at

@@ -37,9 +37,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the DSA library needs ROCm's hipcc to build")
 
 
+# Per-file extra flags. The attention kernel keeps its 128 fp32 output
+# accumulators in ordinary VGPRs (the VGPR form of MFMA), which saves the
+# accumulator-register copies its occasional rescale would otherwise cost.
+EXTRA = {"mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

@@ -111,23 +111,14 @@ Workspace workspace_layout(const LaunchShape &ls)
 {
     Workspace w{};
     const size_t R = (size_t)ls.num_rows;
-    const size_t nc = (size_t)sel_chunks(ls);
+    const size_t stride = (size_t)score_stride(ls);
     const size_t nch = (size_t)att_chunks(ls);
     const size_t hgc = (size_t)att_head_groups(ls);
     size_t off = 0;
-    w.hist = off;
-    off = align256(off + R * kHistBins * sizeof(uint32_t));
-    w.selrow = off;
-    off = align256(off + R * sizeof(SelRow));
-    w.clear_bytes = off;
-    w.n_gt = off;
-    off = align256(off + R * nc * sizeof(uint32_t));
-    w.n_cand = off;
-    off = align256(off + R * nc * sizeof(uint32_t));
-    w.offsets = off;
-    off = align256(off + R * nc * sizeof(uint32_t));
-    w.cand = off;
-    off = align256(off + R * (size_t)ls.max_len * 8);
+    w.spill = off;
+    off = align256(off + R * stride * 8);
+    w.bitmap = off;
+    off = align256(off + R * (stride / 32) * 4);
     w.part_ml = off;
     w.part_o = off;
     if (nch > 1) {
@@ -153,6 +144,14 @@ size_t dsa_workspace_bytes(const dsa_shape *shape)
 
 const char *dsa_last_error(void) { return g_err; }
 
+size_t dsa_score_stride(const dsa_shape *shape)
+{
+    dsa::LaunchShape ls;
+    if (check_shape(shape, &ls) != DSA_OK)
+        return 0;
+    return (size_t)dsa::score_stride(ls);
+}
+
 size_t dsa_bt_entries_needed(size_t seq_len, size_t k, size_t block_size)
 {
     return (seq_len + k) / (block_size ? block_size : 1) + 2;
@@ -172,7 +171,7 @@ int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
         return rc;
     return launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
                                              (const uint16_t *)k_normed, seq_lens, scores,
-                                             nullptr, (hipStream_t)stream),
+                                             (hipStream_t)stream),
                     "index_scores");
 }
 
@@ -190,14 +189,9 @@ int dsa_topk_select(const dsa_shape *shape, const float *scores, const int32_t *
     const dsa::Workspace wl = dsa::workspace_layout(ls);
     if ((rc = check_ws(ws, ws_bytes, wl)) != DSA_OK)
         return rc;
-    hipStream_t st = (hipStream_t)stream;
-    char *wsb = (char *)ws;
-    if ((rc = launched(dsa::launch_clear(wsb, wl.clear_bytes, st), "clear")) ||
-        (rc = launched(dsa::launch_score_hist(ls, scores, seq_lens, (uint32_t *)(wsb + wl.hist), st),
-                       "score_hist")) ||
-        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, st), "select")))
-        return rc;
-    return DSA_OK;
+    return launched(dsa::launch_select(ls, scores, seq_lens, sel, (char *)ws, wl,
+                                       (hipStream_t)stream),
+                    "select");
 }
 
 int dsa_mla_decode(const dsa_shape *shape, const void *q, const uint8_t *kv_cache,
@@ -250,10 +244,8 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, cons
         return rc;
     hipStream_t st = (hipStream_t)stream;
     char *wsb = (char *)ws;
-    if ((rc = launched(dsa::launch_clear(wsb, wl.clear_bytes, st), "clear")) ||
-        (rc = launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
-                                                (const uint16_t *)k_normed, seq_lens, scores,
-                                                (uint32_t *)(wsb + wl.hist), st),
+    if ((rc = launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
+                                                (const uint16_t *)k_normed, seq_lens, scores, st),
                        "index_scores")) ||
         (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, st), "select")) ||
         (rc = launched(dsa::launch_mla_decode(ls, (const uint16_t *)q, kv_cache, block_tables,

@@ -49,14 +49,24 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t word)
     return (hi_bits & 0xFFFF0000u) | (lo_bits >> 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+// The same conversion in one gfx950 instruction (scaled FP8 -> packed bf16
+// with scale 1.0; exact, as every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2_exact(uint32_t word)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 -> bf16, round to nearest even; a NaN stays a (quiet) NaN. Written
+// as a select so it compiles to straight-line code.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x0040u;
+    return (uint16_t)(((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -105,6 +115,36 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     __syncthreads();
     *total = tot;
     return base + x - v;
+}
+
+// Write the 2048-bin histogram held as packed 16-bit LDS counters (bin b in
+// half b & 1 of word b >> 1) as a sparse list: dst[0] = n, then n entries
+// (bin << 16) | count for the non-zero bins in ascending order. blockDim.x ==
+// NT; every thread must call; `scratch` as for block_exclusive_scan.
+template <int NT>
+__device__ __forceinline__ void write_sparse_hist(const uint32_t *hpack, uint32_t *dst,
+                                                  uint32_t *scratch)
+{
+    constexpr int WPT = 1024 / NT; // packed words per thread
+    uint32_t w[WPT];
+    uint32_t nz = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; i++) {
+        w[i] = hpack[threadIdx.x * WPT + i];
+        nz += ((w[i] & 0xFFFFu) != 0) + ((w[i] >> 16) != 0);
+    }
+    uint32_t total;
+    uint32_t at = 1 + block_exclusive_scan<NT>(nz, scratch, &total);
+#pragma unroll
+    for (int i = 0; i < WPT; i++) {
+        const uint32_t bin = 2 * (threadIdx.x * WPT + i);
+        if (w[i] & 0xFFFFu)
+            dst[at++] = (bin << 16) | (w[i] & 0xFFFFu);
+        if (w[i] >> 16)
+            dst[at++] = ((bin + 1) << 16) | (w[i] >> 16);
+    }
+    if (threadIdx.x == 0)
+        dst[0] = total;
 }
 
 } // namespace dsa

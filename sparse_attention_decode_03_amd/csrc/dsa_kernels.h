@@ -20,14 +20,30 @@ struct LaunchShape {
 constexpr int kHistBins = 2048;
 constexpr int kHistShift = 21;
 
-// Selection geometry: rows are cut into chunks of kSelChunk tokens.
-constexpr int kSelChunk = 4096;
 // Attention geometry: a row's selection is cut into chunks of kAttChunk
 // slots; a workgroup covers kAttHeads heads of one chunk.
 constexpr int kAttChunk = 256;
 constexpr int kAttHeads = 64;
 
-inline int sel_chunks(const LaunchShape &ls) { return (ls.max_len + kSelChunk - 1) / kSelChunk; }
+// Row stride of the scores buffer: max_len rounded up to 64 floats, so every
+// row starts 256-byte aligned.
+inline int score_stride(const LaunchShape &ls) { return (ls.max_len + 63) / 64 * 64; }
+
+// Index-score pass geometry: 256-token tiles, each workgroup walks a run of
+// tiles of one sequence (about 512 workgroups in all, 1..64 tiles each).
+constexpr int kIdxTile = 256;
+inline int index_tiles_per_seq(const LaunchShape &ls) { return (ls.max_len + kIdxTile - 1) / kIdxTile; }
+inline int index_tiles_per_wg(const LaunchShape &ls)
+{
+    const long total = (long)index_tiles_per_seq(ls) * ls.num_seqs;
+    int tpw = (int)((total + 511) / 512);
+    return tpw < 1 ? 1 : (tpw > 64 ? 64 : tpw);
+}
+inline int index_wgs_per_seq(const LaunchShape &ls)
+{
+    const int tpw = index_tiles_per_wg(ls);
+    return (index_tiles_per_seq(ls) + tpw - 1) / tpw;
+}
 inline int att_chunks(const LaunchShape &ls)
 {
     const int n = ls.top_k < ls.max_len ? ls.top_k : ls.max_len;
@@ -35,29 +51,19 @@ inline int att_chunks(const LaunchShape &ls)
 }
 inline int att_head_groups(const LaunchShape &ls) { return (ls.num_heads + kAttHeads - 1) / kAttHeads; }
 
-// Per-row selection state in the workspace.
-struct SelRow {
-    uint32_t ticket;     // chunk workgroups of this row that have finished
-    uint32_t thr_key;    // exact threshold key
-    int32_t idx_cut;     // largest selected index among keys equal to thr_key
-    uint32_t pad[5];
-};
-
-// Workspace carve-up (byte offsets, 256-aligned).
+// Workspace carve-up (byte offsets, 256-aligned). Nothing needs zeroing:
+// every part is written before it is read within a call.
 struct Workspace {
-    size_t hist, selrow, clear_bytes; // [0, clear_bytes) is zeroed per call
-    size_t n_gt, n_cand, offsets, cand;
+    size_t spill;   // [R][score_stride] (key, index) candidates past LDS capacity
+    size_t bitmap;  // [R][score_stride / 32] selection bitmaps of long rows
     size_t part_o, part_ml;
     size_t total;
 };
 Workspace workspace_layout(const LaunchShape &ls);
 
-int launch_clear(void *ws, size_t bytes, hipStream_t stream);
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                        uint32_t *hist, hipStream_t stream);
-int launch_score_hist(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
-                      uint32_t *hist, hipStream_t stream);
+                        hipStream_t stream);
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, hipStream_t stream);
 int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,

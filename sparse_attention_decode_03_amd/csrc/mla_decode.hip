@@ -13,14 +13,12 @@
 //    steps of 32 tokens, gathering each token's 512-byte FP8 row through the
 //    block table with coalesced 16-byte loads, dequantising it exactly to
 //    bf16 (E4M3 is a subset of bf16; kv_scale is folded into the logit scale
-//    and the output) and parking the 32 x 512 tile in LDS, token-major, with
-//    an XOR swizzle that keeps both operand reads below free of bank
-//    conflicts.
+//    and the output) and parking the 32 x 512 tile in LDS, token-major, in
+//    padded rows that keep both operand reads below free of bank conflicts.
 //  - QK: S^T[token, head] on 16x16x32 bf16 MFMA, the tile as A (k = latent
-//    dim), Q as B (held in registers for the whole chunk). Tokens are fed to
-//    the MFMA rows in an order that leaves each lane with eight consecutive
-//    tokens of one head -- exactly the k-run the PV operand needs, so the
-//    probabilities never leave registers.
+//    dim), Q as B (staged in LDS once per workgroup). The MFMA output leaves
+//    each lane with eight tokens of one head, which are exactly the k-slots
+//    of that lane's PV operand, so the probabilities never leave registers.
 //  - Online softmax in fp32 (log2 domain, exp2), fixed-order reductions.
 //  - PV: O[head, d] on 16x16x32 bf16 MFMA, P (bf16) as A, the tile as B read
 //    through LDS transpose loads (ds_read_tr16_b64), fp32 accumulators.
@@ -35,18 +33,16 @@ namespace dsa {
 constexpr int kAttThreads = 256;
 constexpr int kStep = 32;          // tokens per LDS tile
 constexpr int kLat = 512;          // latent width
-constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 token row (64)
+constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 latent row (64)
+// LDS rows (a token's bf16 latent, or a head's bf16 query) are padded from
+// 1024 to 1072 bytes (67 chunks). With a 48-byte pad, 16 consecutive rows read
+// at one chunk start 12 words apart modulo the 64 banks (all distinct 4-word
+// groups), and the 4 consecutive rows x 4 eight-byte segments of one
+// transpose read land on 32 distinct banks. Addresses stay a lane base plus
+// compile-time offsets.
+constexpr int kRowStride = kRowChunks + 3; // in 16-byte chunks
 constexpr float kNegInf = -__builtin_huge_valf();
-
-// XOR swizzle of a token row's 16-byte chunks. A QK operand read touches 16
-// rows at one chunk index: the swizzle gives them 16 distinct low-four-bit
-// chunk positions, i.e. all 64 banks. A transpose read touches 4 consecutive
-// rows at one chunk pair: the swizzle moves each row to a different pair, so
-// the 16 lanes' 8-byte reads land on 32 distinct banks.
-__device__ __forceinline__ int tok_swz(int t)
-{
-    return 2 * (t & 3) + 8 * ((t >> 3) & 1) + ((t >> 4) & 1);
-}
+constexpr float kRescaleSlack = 8.0f;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
@@ -58,8 +54,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
-    __shared__ u32x4 tile[kStep * kRowChunks]; // 32 KiB, bf16 token-major
-    __shared__ int rowidx[kAttChunk];          // latent row of each slot, -1 = skip
+    __shared__ u32x4 tile[kStep * kRowStride];      // bf16 tokens x latent, padded rows
+    __shared__ u32x4 qlds[kAttHeads * kRowStride];  // bf16 Q of the 64 heads, padded rows
+    __shared__ int rowidx[kAttChunk];               // latent row of each slot, -1 = skip
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -106,19 +103,18 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         rowidx[tid] = row;
     }
 
-    // Q as the B operand of QK: column = head h_base + n16, k = latent dims
-    // 32*ks + 8*g .. +7.
-    bf16x8 qb[16];
-    {
-        const int h = h_base + n16;
-        const uint16_t *qrow = q + ((int64_t)r * H + (h < H ? h : 0)) * kLat;
+    // Q of the workgroup's 64 heads into LDS (padded head rows).
 #pragma unroll
-        for (int ks = 0; ks < 16; ks++) {
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (h < H)
-                v = *(const u32x4 *)(qrow + 32 * ks + 8 * g);
-            qb[ks] = as_bf16x8(v);
-        }
+    for (int i = 0; i < kAttHeads * kRowChunks / kAttThreads; i++) {
+        const int id = i * kAttThreads + tid;
+        const int hh = id / kRowChunks;
+        const int ch = id % kRowChunks;
+        const int h = hg * kAttHeads + hh;
+        // branch-free: load a valid row, zero it if the head is padding
+        u32x4 v = *(const u32x4 *)(q + ((int64_t)r * H + min(h, H - 1)) * kLat + ch * 8);
+        if (h >= H)
+            v = u32x4{0u, 0u, 0u, 0u};
+        qlds[hh * kRowStride + ch] = v;
     }
     __syncthreads();
 
@@ -138,9 +134,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         for (int i = 0; i < 4; i++) {
             const int k = base - slot0 + 4 * tq + i;
             const int row = (k < kAttChunk) ? rowidx[k] : -1;
-            raw[i] = u32x4{0u, 0u, 0u, 0u};
-            if (row >= 0)
-                raw[i] = *(const u32x4 *)(kv + (int64_t)row * kLat + 16 * dc);
+            // branch-free so the four loads issue back to back: a skipped
+            // slot reads latent row 0 and is zeroed
+            raw[i] = *(const u32x4 *)(kv + (int64_t)max(row, 0) * kLat + 16 * dc);
+            if (row < 0)
+                raw[i] = u32x4{0u, 0u, 0u, 0u};
         }
     };
     // Dequantise (exact) into the bf16 LDS tile.
@@ -149,33 +147,35 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         for (int i = 0; i < 4; i++) {
             const int t = 4 * tq + i;
             u32x4 lo, hi;
-            lo.x = e4m3x2_to_bf16x2<false>(raw[i].x);
-            lo.y = e4m3x2_to_bf16x2<true>(raw[i].x);
-            lo.z = e4m3x2_to_bf16x2<false>(raw[i].y);
-            lo.w = e4m3x2_to_bf16x2<true>(raw[i].y);
-            hi.x = e4m3x2_to_bf16x2<false>(raw[i].z);
-            hi.y = e4m3x2_to_bf16x2<true>(raw[i].z);
-            hi.z = e4m3x2_to_bf16x2<false>(raw[i].w);
-            hi.w = e4m3x2_to_bf16x2<true>(raw[i].w);
-            const int sw = tok_swz(t);
-            tile[t * kRowChunks + ((2 * dc) ^ sw)] = lo;
-            tile[t * kRowChunks + ((2 * dc + 1) ^ sw)] = hi;
+            lo.x = e4m3x2_to_bf16x2_exact<false>(raw[i].x);
+            lo.y = e4m3x2_to_bf16x2_exact<true>(raw[i].x);
+            lo.z = e4m3x2_to_bf16x2_exact<false>(raw[i].y);
+            lo.w = e4m3x2_to_bf16x2_exact<true>(raw[i].y);
+            hi.x = e4m3x2_to_bf16x2_exact<false>(raw[i].z);
+            hi.y = e4m3x2_to_bf16x2_exact<true>(raw[i].z);
+            hi.z = e4m3x2_to_bf16x2_exact<false>(raw[i].w);
+            hi.w = e4m3x2_to_bf16x2_exact<true>(raw[i].w);
+            tile[t * kRowStride + 2 * dc] = lo;
+            tile[t * kRowStride + 2 * dc + 1] = hi;
         }
     };
     // QK, online softmax and PV over the staged tile of step `base`.
     auto compute = [&](int base) {
         // ---- QK: lane ends with head n16, tokens 8g + 4a + v ----
-        floatx4 sacc[2];
+        // ---- QK: S^T[token][head], tile rows as A (token 16a + n16, k =
+        // latent dims 32*ks + 8*g .. +7), Q as B (head wave*16 + n16); the
+        // lane ends with head n16 and tokens 16a + 4g + v (v = 0..3) ----
+        floatx4 sacc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+        {
+            const u32x4 *qrow = qlds + (wave * 16 + n16) * kRowStride + g;
+            const u32x4 *t0row = tile + n16 * kRowStride + g;
+            const u32x4 *t1row = tile + (16 + n16) * kRowStride + g;
 #pragma unroll
-        for (int a = 0; a < 2; a++) {
-            const int trow = 8 * (n16 >> 2) + 4 * a + (n16 & 3);
-            const int sw = tok_swz(trow);
-            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < 16; ks++)
-                acc = mfma16x16x32(as_bf16x8(tile[trow * kRowChunks + ((4 * ks + g) ^ sw)]),
-                                   qb[ks], acc);
-            sacc[a] = acc;
+            for (int ks = 0; ks < 16; ks++) {
+                const bf16x8 qv = as_bf16x8(qrow[4 * ks]);
+                sacc[0] = mfma16x16x32(as_bf16x8(t0row[4 * ks]), qv, sacc[0]);
+                sacc[1] = mfma16x16x32(as_bf16x8(t1row[4 * ks]), qv, sacc[1]);
+            }
         }
         // ---- online softmax (log2 domain) ----
         float z[8];
@@ -183,12 +183,19 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const float v = sacc[j >> 2][j & 3] * qk_log2;
-            z[j] = rowidx[base - slot0 + 8 * g + j] >= 0 ? v : kNegInf;
+            z[j] = rowidx[base - slot0 + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
             mx = __builtin_fmaxf(mx, z[j]);
         }
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = __builtin_fmaxf(m_run, mx);
+        // The reference max moves only when the step's max exceeds it by
+        // more than kRescaleSlack (log2 units): then p <= 2^kRescaleSlack, so
+        // fp32 sums and bf16 probabilities stay well scaled, and O is
+        // rescaled only on rare steps. The rule is a function of the row's
+        // data alone, so results stay bit-reproducible; the partial state
+        // (m_ref, l, O) merges exactly as with the true max.
+        const bool move = mx > m_run + kRescaleSlack;
+        const float m_new = move ? mx : m_run;
         const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
         const float alpha = exp2f(m_run - m_use);
         float p[8];
@@ -201,10 +208,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         rs += __shfl_xor(rs, 16, kWave);
         rs += __shfl_xor(rs, 32, kWave);
         l_run = __builtin_fmaf(l_run, alpha, rs);
-        // O rows are heads 4g + v: rescale them by their own alpha, but only
-        // when some head's maximum grew (otherwise every alpha is exactly 1,
-        // or O is still zero, and the multiply would change nothing)
-        const bool grew = __ballot(m_new > m_run && m_run != kNegInf) != 0;
+        // O rows are heads 4g + v: rescale them by their own alpha, only on a
+        // step where some head's reference moved (otherwise every alpha is
+        // exactly 1, or O is still zero, and the multiply changes nothing)
+        const bool grew = __ballot(move && m_run != kNegInf) != 0;
         m_run = m_new;
         if (grew) {
             float av[4];
@@ -225,19 +232,17 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         pw.z = pack_bf16x2(p[4], p[5]);
         pw.w = pack_bf16x2(p[6], p[7]);
         const bf16x8 pa = as_bf16x8(pw);
-        // ---- PV: B = tile^T through transpose loads ----
-        const int tr_row0 = 8 * g + (n16 >> 2); // tokens 8g + 0..3
-        const int tr_row1 = tr_row0 + 4;        // tokens 8g + 4..7
-        const int sw0 = tok_swz(tr_row0);
-        const int sw1 = tok_swz(tr_row1);
-        const int half = (n16 & 1) * 4; // shorts within the chunk
+        // ---- PV: O[head][d] += P[head][token] C[token][d]; P as A (k-slot
+        // j <-> token 16(j>>2) + 4g + (j&3), exactly the tokens this lane's
+        // softmax holds), the tile as B through two transpose loads of 4
+        // consecutive rows each: lane n16 receives latent column 16*nt + n16 ----
+        const char *tb = (const char *)tile;
+        const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3);
+        const char *p1 = p0 + 16 * (kRowStride * 16);
 #pragma unroll
         for (int nt = 0; nt < 32; nt++) {
-            const int ch = 2 * nt + ((n16 & 3) >> 1);
-            const short *p0 = (const short *)&tile[tr_row0 * kRowChunks + (ch ^ sw0)] + half;
-            const short *p1 = (const short *)&tile[tr_row1 * kRowChunks + (ch ^ sw1)] + half;
-            const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p0);
-            const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)p1);
+            const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p0 + 32 * nt));
+            const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p1 + 32 * nt));
             typedef short shortx8 __attribute__((ext_vector_type(8)));
             const shortx8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
             o[nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, bb), o[nt]);
@@ -320,20 +325,35 @@ __global__ __launch_bounds__(128) void k_mla_merge(const float *__restrict__ par
     const int d = threadIdx.x * 4;
     float m_acc = kNegInf, l_acc = 0.0f;
     floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < nch; c++) {
-        const int64_t pi = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads + hl;
-        const float2 ml = part_ml[pi];
-        const floatx4 ov = *(const floatx4 *)(part_o + pi * kLat + d);
-        const float m_new = __builtin_fmaxf(m_acc, ml.x);
-        if (m_new == kNegInf)
-            continue;
-        const float a = exp2f(m_acc - m_new);
-        const float b = exp2f(ml.x - m_new);
-        l_acc = __builtin_fmaf(ml.y, b, l_acc * a);
+    // partials are loaded in unrolled batches (independent loads in flight),
+    // then folded strictly in chunk order
+    constexpr int kB = 8;
+    for (int c0 = 0; c0 < nch; c0 += kB) {
+        float2 ml[kB];
+        floatx4 ov[kB];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            acc[i] = __builtin_fmaf(ov[i], b, acc[i] * a);
-        m_acc = m_new;
+        for (int k = 0; k < kB; k++) {
+            // branch-free: chunks past the row's last re-read its last one
+            const int64_t pi =
+                (((int64_t)r * hg_count + hg) * nch_max + min(c0 + k, nch - 1)) * kAttHeads + hl;
+            ml[k] = part_ml[pi];
+            ov[k] = *(const floatx4 *)(part_o + pi * kLat + d);
+        }
+#pragma unroll
+        for (int k = 0; k < kB; k++) {
+            if (c0 + k >= nch)
+                break;
+            const float m_new = __builtin_fmaxf(m_acc, ml[k].x);
+            if (m_new == kNegInf)
+                continue;
+            const float a = exp2f(m_acc - m_new);
+            const float b = exp2f(ml[k].x - m_new);
+            l_acc = __builtin_fmaf(ml[k].y, b, l_acc * a);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                acc[i] = __builtin_fmaf(ov[k][i], b, acc[i] * a);
+            m_acc = m_new;
+        }
     }
     const float inv = l_acc > 0.0f ? kv_scale / l_acc : 0.0f;
     uint16_t *orow = out + ((int64_t)r * H + h) * kLat + d;

@@ -6,85 +6,34 @@
 // (pools of one token); -0.0 equals +0.0. Output: the selected ids in
 // ascending order, -1 past min(top_k, L_r).
 //
-// Radix selection on the order-preserving 32-bit key of each score:
-//  1. A 2048-bin histogram of the key's top 11 bits per row (fused into the
-//     scoring pass by dsa_decode_k; a separate pass for dsa_topk_select).
-//  2. k_select_candidates, one workgroup per 4096-token chunk of a row: every
-//     workgroup finds the bin b* that holds the k-th largest key, counts the
-//     keys above b* in its chunk and compacts the keys inside b* into the
-//     chunk's own candidate region. The last workgroup of the row (an
-//     atomic ticket; no workgroup ever waits) resolves the exact threshold
-//     key T and the index cut among keys equal to T with four more radix
-//     passes over the candidates, then turns per-chunk selected counts into
-//     output offsets.
-//  3. k_select_compact, again one workgroup per chunk: writes the selected
-//     ids of its chunk in ascending order at the chunk's offset.
+// One workgroup of 1024 threads owns one row, so no step ever waits on
+// another workgroup. Radix selection on the order-preserving 32-bit key of
+// each score:
+//  1. sweep 1: a 2048-bin histogram of the key's top 11 bits (four LDS copies
+//     to spread atomic contention); the bin b* holding the k-th largest key
+//     follows from a suffix scan;
+//  2. sweep 2: keys above b* go straight into a bitmap of the row (one wave
+//     ballot builds eight bitmap words, no atomics); keys inside b* are the
+//     candidates, appended to LDS (or to a workspace spill past capacity);
+//  3. four radix passes over the candidates resolve the exact threshold key T
+//     and, among keys equal to T, the largest selected index;
+//  4. the selected candidates join the bitmap, and a block-wide scan of the
+//     bitmap's popcounts writes the ids in ascending order.
+// Sweeps read the row with 16-byte loads, two batches in flight.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
 namespace dsa {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelPerThread = kSelChunk / kSelThreads; // 16
-
-__global__ void k_clear(u32x4 *p, size_t n16)
-{
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = u32x4{0u, 0u, 0u, 0u};
-}
-
-int launch_clear(void *ws, size_t bytes, hipStream_t stream)
-{
-    const size_t n16 = bytes / 16;
-    if (n16 == 0)
-        return 0;
-    size_t blocks = (n16 + 255) / 256;
-    if (blocks > 1024)
-        blocks = 1024;
-    hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4 *)ws, n16);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// Histogram of the top 11 key bits of scores[r, 0..L) (rows with L > top_k).
-__global__ __launch_bounds__(kSelThreads) void k_score_hist(const float *__restrict__ scores,
-                                                            const int32_t *__restrict__ seq_lens,
-                                                            uint32_t *__restrict__ hist,
-                                                            int max_len, int top_k)
-{
-    __shared__ uint32_t h[kHistBins];
-    const int r = blockIdx.y;
-    const int L = min(max(seq_lens[r], 0), max_len);
-    const int base = blockIdx.x * kSelChunk;
-    if (L <= top_k || base >= L)
-        return;
-    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads)
-        h[i] = 0u;
-    __syncthreads();
-    const float *row = scores + (int64_t)r * max_len;
-    for (int i = 0; i < kSelPerThread; i++) {
-        const int t = base + i * kSelThreads + threadIdx.x;
-        if (t < L)
-            atomicAdd(&h[score_key(row[t]) >> kHistShift], 1u);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads)
-        if (h[i])
-            atomicAdd(&hist[(int64_t)r * kHistBins + i], h[i]);
-}
-
-int launch_score_hist(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
-                      uint32_t *hist, hipStream_t stream)
-{
-    dim3 grid(sel_chunks(ls), ls.num_rows);
-    hipLaunchKernelGGL(k_score_hist, grid, dim3(kSelThreads), 0, stream, scores, seq_lens, hist,
-                       ls.max_len, ls.top_k);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / kWave;
+constexpr int kVecBatch = 8;           // float4 loads per thread per batch
+constexpr int kCandCap = 6144;         // candidates kept in LDS (48 KiB)
+constexpr int kBitmapLdsWords = 12288; // rows up to 393216 tokens keep the bitmap in LDS
 
 // Shared state of one block-wide bin search.
 struct BinSearch {
-    uint32_t scan[kSelThreads / kWave + 1];
+    uint32_t scan[kRowWaves + 1];
     uint32_t bin;
     uint32_t before;
 };
@@ -97,7 +46,7 @@ template <bool Descending>
 __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSearch *bs,
                              uint32_t *before)
 {
-    const int bpt = nbins / kSelThreads;
+    const int bpt = (nbins + kRowThreads - 1) / kRowThreads;
     const int tid = threadIdx.x;
     if (tid == 0) {
         bs->bin = 0u; // defined result even for an inconsistent histogram
@@ -106,12 +55,15 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
     uint32_t local = 0;
     for (int i = 0; i < bpt; i++) {
         const int p = tid * bpt + i;
-        local += h[Descending ? nbins - 1 - p : p];
+        if (p < nbins)
+            local += h[Descending ? nbins - 1 - p : p];
     }
     uint32_t total;
-    uint32_t run = block_exclusive_scan<kSelThreads>(local, bs->scan, &total);
+    uint32_t run = block_exclusive_scan<kRowThreads>(local, bs->scan, &total);
     for (int i = 0; i < bpt; i++) {
         const int p = tid * bpt + i;
+        if (p >= nbins)
+            break;
         const int b = Descending ? nbins - 1 - p : p;
         const uint32_t c = h[b];
         if (run < need && run + c >= need) {
@@ -127,235 +79,227 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
     return b;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select_candidates(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
-    const uint32_t *__restrict__ hist, SelRow *__restrict__ rows, uint32_t *__restrict__ n_gt,
-    uint32_t *__restrict__ n_cand, uint32_t *__restrict__ offsets, u32x2 *__restrict__ cand,
-    int max_len, int top_k, int nc_max)
+// Spread the 8 bits of x to bit positions 0, 4, 8, ..., 28.
+__device__ __forceinline__ uint32_t spread8(uint32_t x)
 {
-    __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t chunk_cnt[1024];
-    __shared__ uint32_t chunk_cand[1024];
+    x = (x | (x << 12)) & 0x000F000Fu;
+    x = (x | (x << 6)) & 0x03030303u;
+    x = (x | (x << 3)) & 0x11111111u;
+    return x;
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_select_row(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
+    int32_t *__restrict__ sel, u32x2 *__restrict__ spill, uint32_t *__restrict__ gbitmap,
+    int max_len, int stride, int top_k)
+{
+    __shared__ uint32_t hsub[4][kHistBins];
+    __shared__ u32x2 cbuf[kCandCap];
+    __shared__ uint32_t lbitmap[kBitmapLdsWords];
     __shared__ BinSearch bs;
-    __shared__ uint32_t scan[kSelThreads / kWave + 1];
-    __shared__ int is_last;
+    __shared__ uint32_t ccount;
 
-    const int r = blockIdx.y;
-    const int c = blockIdx.x;
+    const int r = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
     const int L = min(max(seq_lens[r], 0), max_len);
-    if (L <= top_k)
-        return;
-    const int nc = (L + kSelChunk - 1) / kSelChunk;
-    if (c >= nc)
-        return;
-    SelRow *st = rows + r;
+    int32_t *out = sel + (int64_t)r * top_k;
 
-    // ---- the bin b* of the top_k-th largest key ----
-    for (int i = tid; i < kHistBins; i += kSelThreads)
-        h[i] = hist[(int64_t)r * kHistBins + i];
-    __syncthreads();
-    uint32_t above;
-    const uint32_t bstar = find_bin<true>(h, kHistBins, (uint32_t)top_k, &bs, &above);
-    const uint32_t need = (uint32_t)top_k - above; // keys to take from bin b*
+    if (L <= top_k) { // every token is selected; slots past L are padding
+        for (int slot = tid; slot < top_k; slot += kRowThreads)
+            out[slot] = slot < L ? slot : -1;
+        return;
+    }
 
-    // ---- this chunk: count keys above b*, gather keys inside b* into the
-    //      chunk's own candidate region (no cross-workgroup atomics) ----
-    const float *row = scores + (int64_t)r * max_len;
-    u32x2 *rc = cand + (int64_t)r * max_len;
-    uint32_t keys[kSelPerThread];
-    uint32_t inmask = 0, gt = 0, nin = 0;
+    const float4 *row4 = (const float4 *)(scores + (int64_t)r * stride);
+    const int nvec = (L + 3) / 4; // float4s covering [0, L) (all inside the row stride)
+    constexpr int kBatchTok = kRowThreads * kVecBatch * 4;
+    // Two batches of kVecBatch float4 per thread in flight; f(t, v) runs for
+    // the float4 v holding tokens t .. t+3 (t a multiple of 4; entries at or
+    // past L are masked by f).
+    auto sweep = [&](auto &&f) {
+        float4 a[kVecBatch], b[kVecBatch];
+        auto load = [&](float4(&x)[kVecBatch], int base) {
 #pragma unroll
-    for (int i = 0; i < kSelPerThread; i++) {
-        const int t = c * kSelChunk + i * kSelThreads + tid;
-        keys[i] = 0;
-        if (t < L) {
-            keys[i] = score_key(row[t]);
-            const uint32_t b = keys[i] >> kHistShift;
-            gt += b > bstar;
-            if (b == bstar) {
-                inmask |= 1u << i;
-                nin++;
-            }
-        }
-    }
-    uint32_t n_in_chunk;
-    uint32_t at = block_exclusive_scan<kSelThreads>(nin, scan, &n_in_chunk);
+            for (int k = 0; k < kVecBatch; k++)
+                x[k] = row4[min(base / 4 + k * kRowThreads + tid, nvec - 1)];
+        };
+        auto use = [&](const float4(&x)[kVecBatch], int base) {
 #pragma unroll
-    for (int i = 0; i < kSelPerThread; i++)
-        if (inmask & (1u << i))
-            rc[c * kSelChunk + at++] = u32x2{keys[i], (uint32_t)(c * kSelChunk + i * kSelThreads + tid)};
-    uint32_t n_gt_chunk;
-    block_exclusive_scan<kSelThreads>(gt, scan, &n_gt_chunk);
-    if (tid == 0) {
-        n_gt[(int64_t)r * nc_max + c] = n_gt_chunk;
-        n_cand[(int64_t)r * nc_max + c] = n_in_chunk;
-    }
-
-    // ---- the last workgroup of the row resolves the threshold ----
-    __threadfence();
-    __syncthreads();
-    if (tid == 0)
-        is_last = atomicAdd(&st->ticket, 1u) == (uint32_t)(nc - 1);
-    __syncthreads();
-    if (!is_last)
-        return;
-    __threadfence();
-    for (int i = tid; i < nc; i += kSelThreads) {
-        chunk_cand[i] = min(__hip_atomic_load(&n_cand[(int64_t)r * nc_max + i], __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT),
-                            (uint32_t)kSelChunk);
-        chunk_cnt[i] = __hip_atomic_load(&n_gt[(int64_t)r * nc_max + i], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // visit every candidate of the row (chunk regions, in any order)
-    auto for_each = [&](auto &&f) {
-        for (int cc = 0; cc < nc; cc++) {
-            const uint32_t n = chunk_cand[cc];
-            for (uint32_t i = tid; i < n; i += kSelThreads)
-                f(rc[cc * kSelChunk + i]);
+            for (int k = 0; k < kVecBatch; k++)
+                f(base + 4 * (k * kRowThreads + tid), x[k]);
+        };
+        load(a, 0);
+        for (int base = 0; base < L; base += 2 * kBatchTok) {
+            if (base + kBatchTok < L)
+                load(b, base + kBatchTok);
+            use(a, base);
+            if (base + kBatchTok >= L)
+                break;
+            if (base + 2 * kBatchTok < L)
+                load(a, base + 2 * kBatchTok);
+            use(b, base + kBatchTok);
         }
     };
 
-    // pass A: key bits [20:10] of the candidates, descending
-    for (int i = tid; i < kHistBins; i += kSelThreads)
-        h[i] = 0u;
+    // ---- sweep 1: histogram of the top 11 key bits ----
+    for (int i = tid; i < 4 * kHistBins; i += kRowThreads)
+        (&hsub[0][0])[i] = 0u;
     __syncthreads();
-    for_each([&](u32x2 e) { atomicAdd(&h[(e.x >> 10) & 0x7FFu], 1u); });
+    uint32_t *myh = hsub[wave & 3];
+    sweep([&](int t, float4 v) {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            if (t + j < L)
+                atomicAdd(&myh[score_key(e[j]) >> kHistShift], 1u);
+    });
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += kRowThreads)
+        hsub[0][i] += hsub[1][i] + hsub[2][i] + hsub[3][i];
+    if (tid == 0)
+        ccount = 0u;
+    __syncthreads();
+    uint32_t above;
+    const uint32_t bstar = find_bin<true>(hsub[0], kHistBins, (uint32_t)top_k, &bs, &above);
+    const uint32_t need = (uint32_t)top_k - above; // keys to take from bin b*
+
+    // ---- sweep 2: keys above b* -> bitmap; keys inside b* -> candidates ----
+    const int nwords = (L + 31) / 32;
+    uint32_t *bm = nwords <= kBitmapLdsWords ? lbitmap : gbitmap + (int64_t)r * (stride / 32);
+    u32x2 *rspill = spill + (int64_t)r * stride;
+    sweep([&](int t, float4 v) {
+        const float e[4] = {v.x, v.y, v.z, v.w};
+        uint64_t ab[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const bool valid = t + j < L;
+            const uint32_t key = score_key(e[j]);
+            const uint32_t bin = key >> kHistShift;
+            ab[j] = __ballot(valid && bin > bstar);
+            const bool in = valid && bin == bstar;
+            const uint64_t cm = __ballot(in);
+            if (cm) {
+                const int leader = __ffsll((unsigned long long)cm) - 1;
+                uint32_t pos = 0;
+                if (lane == leader)
+                    pos = atomicAdd(&ccount, (uint32_t)__popcll(cm));
+                pos = __shfl(pos, leader, kWave);
+                if (in) {
+                    const uint32_t at = pos + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
+                    const u32x2 ent = u32x2{key, (uint32_t)(t + j)};
+                    if (at < (uint32_t)kCandCap)
+                        cbuf[at] = ent;
+                    else if (at < (uint32_t)L)
+                        rspill[at] = ent;
+                }
+            }
+        }
+        // The wave's 256 tokens start at a multiple of 256: lane q < 8 writes
+        // bitmap word q (tokens 32q..32q+31 = lanes 8q..8q+7, 4 elements
+        // each). Every word of [0, nwords) is written exactly once.
+        const int s0 = t - 4 * lane;
+        if (lane < 8 && s0 + 32 * lane < L) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                word |= spread8((uint32_t)(ab[j] >> (8 * lane)) & 0xFFu) << j;
+            bm[(s0 >> 5) + lane] = word;
+        }
+    });
+    __syncthreads();
+    const uint32_t m = min(ccount, (uint32_t)L);
+    auto cand_at = [&](uint32_t i) -> u32x2 { return i < (uint32_t)kCandCap ? cbuf[i] : rspill[i]; };
+
+    // ---- radix passes over the candidates ----
+    uint32_t *h = hsub[0];
+    auto clear_h = [&]() {
+        for (int i = tid; i < kHistBins; i += kRowThreads)
+            h[i] = 0u;
+        __syncthreads();
+    };
+    // pass A: key bits [20:10], descending
+    clear_h();
+    for (uint32_t i = tid; i < m; i += kRowThreads)
+        atomicAdd(&h[(cand_at(i).x >> 10) & 0x7FFu], 1u);
     __syncthreads();
     uint32_t bef;
     const uint32_t a_bin = find_bin<true>(h, 2048, need, &bs, &bef);
     const uint32_t need_a = need - bef;
     const uint32_t hi21 = (bstar << 11) | a_bin; // key >> 10
-
     // pass B: key bits [9:0] among key >> 10 == hi21, descending
-    for (int i = tid; i < kHistBins; i += kSelThreads)
-        h[i] = 0u;
-    __syncthreads();
-    for_each([&](u32x2 e) {
-        if ((e.x >> 10) == hi21)
-            atomicAdd(&h[e.x & 0x3FFu], 1u);
-    });
+    clear_h();
+    for (uint32_t i = tid; i < m; i += kRowThreads) {
+        const uint32_t k = cand_at(i).x;
+        if ((k >> 10) == hi21)
+            atomicAdd(&h[k & 0x3FFu], 1u);
+    }
     __syncthreads();
     const uint32_t b_bin = find_bin<true>(h, 1024, need_a, &bs, &bef);
     const uint32_t need_t = need_a - bef; // keys equal to T to take
     const uint32_t eq_count = h[b_bin];
     const uint32_t T = (hi21 << 10) | b_bin;
     __syncthreads();
-
     int32_t cut = 0x7FFFFFFF;
     if (need_t < eq_count) {
         // pass C: index bits [21:11] among keys == T, ascending
-        for (int i = tid; i < kHistBins; i += kSelThreads)
-            h[i] = 0u;
-        __syncthreads();
-        for_each([&](u32x2 e) {
+        clear_h();
+        for (uint32_t i = tid; i < m; i += kRowThreads) {
+            const u32x2 e = cand_at(i);
             if (e.x == T)
                 atomicAdd(&h[(e.y >> 11) & 0x7FFu], 1u);
-        });
+        }
         __syncthreads();
         const uint32_t c_bin = find_bin<false>(h, 2048, need_t, &bs, &bef);
         const uint32_t need_c = need_t - bef;
         // pass D: index bits [10:0] among keys == T in index block c_bin
-        for (int i = tid; i < kHistBins; i += kSelThreads)
-            h[i] = 0u;
-        __syncthreads();
-        for_each([&](u32x2 e) {
+        clear_h();
+        for (uint32_t i = tid; i < m; i += kRowThreads) {
+            const u32x2 e = cand_at(i);
             if (e.x == T && (e.y >> 11) == c_bin)
                 atomicAdd(&h[e.y & 0x7FFu], 1u);
-        });
+        }
         __syncthreads();
         const uint32_t d_bin = find_bin<false>(h, 2048, need_c, &bs, &bef);
         cut = (int32_t)((c_bin << 11) | d_bin);
     }
 
-    // per-chunk selected counts -> exclusive offsets
-    for_each([&](u32x2 e) {
+    // ---- selected candidates join the bitmap ----
+    for (uint32_t i = tid; i < m; i += kRowThreads) {
+        const u32x2 e = cand_at(i);
         if (e.x > T || (e.x == T && (int32_t)e.y <= cut))
-            atomicAdd(&chunk_cnt[e.y / kSelChunk], 1u);
-    });
+            atomicOr(&bm[e.y >> 5], 1u << (e.y & 31));
+    }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t run = 0;
-        for (int i = 0; i < nc; i++) {
-            offsets[(int64_t)r * nc_max + i] = run;
-            run += chunk_cnt[i];
-        }
-        st->thr_key = T;
-        st->idx_cut = cut;
-    }
-}
 
-__global__ __launch_bounds__(kSelThreads) void k_select_compact(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
-    const SelRow *__restrict__ rows, const uint32_t *__restrict__ offsets,
-    int32_t *__restrict__ sel, int max_len, int top_k, int nc_max)
-{
-    __shared__ uint32_t scan[kSelThreads / kWave + 1];
-    const int r = blockIdx.y;
-    const int c = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int L = min(max(seq_lens[r], 0), max_len);
-    int32_t *out = sel + (int64_t)r * top_k;
-
-    if (L <= top_k) {
-        // every token is selected; slots past L are padding
-        for (int i = 0; i < kSelPerThread; i++) {
-            const int slot = c * kSelChunk + i * kSelThreads + tid;
-            if (slot < top_k)
-                out[slot] = slot < L ? slot : -1;
-        }
-        return;
-    }
-    const int nc = (L + kSelChunk - 1) / kSelChunk;
-    if (c >= nc)
-        return;
-    const uint32_t T = rows[r].thr_key;
-    const int32_t cut = rows[r].idx_cut;
-    const float *row = scores + (int64_t)r * max_len;
-    const int t0 = c * kSelChunk + tid * kSelPerThread;
-    uint32_t flags = 0;
+    // ---- ascending ids: block scan of the bitmap's popcounts ----
+    const int wpt = (nwords + kRowThreads - 1) / kRowThreads;
+    const int w0 = tid * wpt;
     uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kSelPerThread; i++) {
-        const int t = t0 + i;
-        if (t < L) {
-            const uint32_t k = score_key(row[t]);
-            if (k > T || (k == T && t <= cut)) {
-                flags |= 1u << i;
-                cnt++;
-            }
+    for (int i = 0; i < wpt; i++)
+        if (w0 + i < nwords)
+            cnt += __popc(bm[w0 + i]);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kRowThreads>(cnt, bs.scan, &total);
+    for (int i = 0; i < wpt; i++) {
+        if (w0 + i >= nwords)
+            break;
+        uint32_t word = bm[w0 + i];
+        while (word && pos < (uint32_t)top_k) {
+            const int bit = __ffs(word) - 1;
+            out[pos++] = 32 * (w0 + i) + bit;
+            word &= word - 1;
         }
     }
-    uint32_t total;
-    uint32_t pos = block_exclusive_scan<kSelThreads>(cnt, scan, &total) +
-                   offsets[(int64_t)r * nc_max + c];
-#pragma unroll
-    for (int i = 0; i < kSelPerThread; i++)
-        if ((flags & (1u << i)) && pos < (uint32_t)top_k)
-            out[pos++] = t0 + i;
 }
 
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, hipStream_t stream)
 {
-    const int nc = sel_chunks(ls);
-    const uint32_t *hist = (const uint32_t *)(ws + wl.hist);
-    SelRow *rows = (SelRow *)(ws + wl.selrow);
-    uint32_t *n_gt = (uint32_t *)(ws + wl.n_gt);
-    uint32_t *n_cand = (uint32_t *)(ws + wl.n_cand);
-    uint32_t *offs = (uint32_t *)(ws + wl.offsets);
-    u32x2 *cand = (u32x2 *)(ws + wl.cand);
-    hipLaunchKernelGGL(k_select_candidates, dim3(nc, ls.num_rows), dim3(kSelThreads), 0, stream,
-                       scores, seq_lens, hist, rows, n_gt, n_cand, offs, cand, ls.max_len,
-                       ls.top_k, nc);
-    if (hipGetLastError() != hipSuccess)
-        return -1;
-    const int ncc = (ls.max_len > ls.top_k ? ls.max_len : ls.top_k);
-    const int gx = (ncc + kSelChunk - 1) / kSelChunk;
-    hipLaunchKernelGGL(k_select_compact, dim3(gx, ls.num_rows), dim3(kSelThreads), 0, stream,
-                       scores, seq_lens, rows, offs, sel, ls.max_len, ls.top_k, nc);
+    hipLaunchKernelGGL(k_select_row, dim3(ls.num_rows), dim3(kRowThreads), 0, stream, scores,
+                       seq_lens, sel, (u32x2 *)(ws + wl.spill), (uint32_t *)(ws + wl.bitmap),
+                       ls.max_len, score_stride(ls), ls.top_k);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -29,6 +29,7 @@ EXPORTS = (
     "dsa_topk_select",
     "dsa_mla_decode",
     "dsa_decode_k",
+    "dsa_score_stride",
     "dsa_bt_entries_needed",
     "dsa_last_error",
 )
@@ -103,6 +104,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_mla_decode.restype = i32
     lib.dsa_decode_k.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P, sz, P]
     lib.dsa_decode_k.restype = i32
+    lib.dsa_score_stride.argtypes = [S]
+    lib.dsa_score_stride.restype = sz
     lib.dsa_bt_entries_needed.argtypes = [sz, sz, sz]
     lib.dsa_bt_entries_needed.restype = sz
     lib.dsa_last_error.argtypes = []
@@ -140,6 +143,11 @@ def _stream(stream) -> Optional[int]:
 
 def workspace_bytes(shape: Shape) -> int:
     return int(load().dsa_workspace_bytes(ctypes.byref(shape)))
+
+
+def score_stride(shape: Shape) -> int:
+    """Row stride (floats) of a scores buffer for `shape`."""
+    return int(load().dsa_score_stride(ctypes.byref(shape)))
 
 
 def bt_entries_needed(seq_len: int, k: int, block_size: int) -> int:
@@ -197,7 +205,7 @@ class DeviceStep:
         self.block_tables = torch.from_numpy(inputs["block_tables"]).to(dev)
         self.seq_lens = torch.from_numpy(inputs["seq_lens"]).to(dev)
         R = sh.num_rows
-        self.scores = torch.empty((R, sh.max_len), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((R, score_stride(sh)), dtype=torch.float32, device=dev)
         self.sel = torch.empty((R, sh.top_k), dtype=torch.int32, device=dev)
         self.out = torch.empty((R, sh.num_heads, sh.latent_dim), dtype=torch.int16, device=dev)
         nb = workspace_bytes(sh)

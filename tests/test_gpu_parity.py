@@ -99,7 +99,10 @@ def test_massive_ties_and_signed_zeros_in_selection():
     shape = dsa.Shape(num_seqs=R, rows_per_seq=1, num_heads=8, latent_dim=512, index_heads=4,
                       index_dim=64, top_k=top_k, page_size=64, max_len=max_len,
                       k_capacity=max_len, max_blocks_per_seq=(max_len + 63) // 64, num_pages=1)
-    d_sc = torch.from_numpy(sc).cuda()
+    stride = dsa.score_stride(shape)
+    padded = np.full((R, stride), np.nan, np.float32)  # past max_len: never read
+    padded[:, :max_len] = sc
+    d_sc = torch.from_numpy(padded).cuda()
     d_len = torch.from_numpy(lens).cuda()
     d_sel = torch.full((R, top_k), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(dsa.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
