@@ -115,9 +115,15 @@ Workspace workspace_layout(const LaunchShape &ls)
     const size_t nch = (size_t)att_chunks(ls);
     const size_t hgc = (size_t)att_head_groups(ls);
     size_t off = 0;
-    w.spill = off;
+    w.cand = off;
     off = align256(off + R * stride * 8);
     w.bitmap = off;
+    off = align256(off + R * (stride / 32) * 4);
+    w.cnt = off;
+    off = align256(off + R * (size_t)dsa::sel_slices(ls) * 4);
+    w.gm4 = off;
+    off = align256(off + R * (stride / 4) * 4);
+    w.gm32 = off;
     off = align256(off + R * (stride / 32) * 4);
     w.part_ml = off;
     w.part_o = off;
@@ -171,7 +177,7 @@ int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
         return rc;
     return launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
                                              (const uint16_t *)k_normed, seq_lens, scores,
-                                             (hipStream_t)stream),
+                                             nullptr, nullptr, (hipStream_t)stream),
                     "index_scores");
 }
 
@@ -189,7 +195,7 @@ int dsa_topk_select(const dsa_shape *shape, const float *scores, const int32_t *
     const dsa::Workspace wl = dsa::workspace_layout(ls);
     if ((rc = check_ws(ws, ws_bytes, wl)) != DSA_OK)
         return rc;
-    return launched(dsa::launch_select(ls, scores, seq_lens, sel, (char *)ws, wl,
+    return launched(dsa::launch_select(ls, scores, seq_lens, sel, (char *)ws, wl, false,
                                        (hipStream_t)stream),
                     "select");
 }
@@ -245,9 +251,12 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, cons
     hipStream_t st = (hipStream_t)stream;
     char *wsb = (char *)ws;
     if ((rc = launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
-                                                (const uint16_t *)k_normed, seq_lens, scores, st),
+                                                (const uint16_t *)k_normed, seq_lens, scores,
+                                                (uint32_t *)(wsb + wl.gm4),
+                                                (uint32_t *)(wsb + wl.gm32), st),
                        "index_scores")) ||
-        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, st), "select")) ||
+        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, true, st),
+                       "select")) ||
         (rc = launched(dsa::launch_mla_decode(ls, (const uint16_t *)q, kv_cache, block_tables,
                                               seq_lens, sel, kv_scale, sm_scale, (uint16_t *)out,
                                               wsb, wl, st),

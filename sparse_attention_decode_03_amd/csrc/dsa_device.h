@@ -117,34 +117,4 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     return base + x - v;
 }
 
-// Write the 2048-bin histogram held as packed 16-bit LDS counters (bin b in
-// half b & 1 of word b >> 1) as a sparse list: dst[0] = n, then n entries
-// (bin << 16) | count for the non-zero bins in ascending order. blockDim.x ==
-// NT; every thread must call; `scratch` as for block_exclusive_scan.
-template <int NT>
-__device__ __forceinline__ void write_sparse_hist(const uint32_t *hpack, uint32_t *dst,
-                                                  uint32_t *scratch)
-{
-    constexpr int WPT = 1024 / NT; // packed words per thread
-    uint32_t w[WPT];
-    uint32_t nz = 0;
-#pragma unroll
-    for (int i = 0; i < WPT; i++) {
-        w[i] = hpack[threadIdx.x * WPT + i];
-        nz += ((w[i] & 0xFFFFu) != 0) + ((w[i] >> 16) != 0);
-    }
-    uint32_t total;
-    uint32_t at = 1 + block_exclusive_scan<NT>(nz, scratch, &total);
-#pragma unroll
-    for (int i = 0; i < WPT; i++) {
-        const uint32_t bin = 2 * (threadIdx.x * WPT + i);
-        if (w[i] & 0xFFFFu)
-            dst[at++] = (bin << 16) | (w[i] & 0xFFFFu);
-        if (w[i] >> 16)
-            dst[at++] = ((bin + 1) << 16) | (w[i] >> 16);
-    }
-    if (threadIdx.x == 0)
-        dst[0] = total;
-}
-
 } // namespace dsa

@@ -16,9 +16,11 @@ struct LaunchShape {
     int top_k, page_size, max_len, k_capacity, max_blocks, num_pages;
 };
 
-// Bins of the first selection histogram (top 11 bits of the score key).
+// Selection: radix digits of up to 11 bits (2048 bins); the filter pass
+// cuts each row into slices of kSelSlice tokens.
 constexpr int kHistBins = 2048;
-constexpr int kHistShift = 21;
+constexpr int kSelSlice = 4096;
+inline int sel_slices(const LaunchShape &ls) { return (ls.max_len + kSelSlice - 1) / kSelSlice; }
 
 // Attention geometry: a row's selection is cut into chunks of kAttChunk
 // slots; a workgroup covers kAttHeads heads of one chunk.
@@ -54,18 +56,26 @@ inline int att_head_groups(const LaunchShape &ls) { return (ls.num_heads + kAttH
 // Workspace carve-up (byte offsets, 256-aligned). Nothing needs zeroing:
 // every part is written before it is read within a call.
 struct Workspace {
-    size_t spill;   // [R][score_stride] (key, index) candidates past LDS capacity
+    size_t cand;    // [R][score_stride] (key, index) selection candidates
     size_t bitmap;  // [R][score_stride / 32] selection bitmaps of long rows
+    size_t cnt;     // [R][sel_slices] candidates per slice
+    size_t gm4;     // [R][score_stride / 4] max key of each 4-token group
+    size_t gm32;    // [R][score_stride / 32] max key of each 32-token group
     size_t part_o, part_ml;
     size_t total;
 };
 Workspace workspace_layout(const LaunchShape &ls);
 
+// gm4 / gm32 null: scores only. Otherwise the pass also writes the group
+// maxima the selection threshold is taken from.
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                        hipStream_t stream);
+                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream);
+// have_group_max: the group maxima in the workspace were written by the
+// index pass of the same call; otherwise the selection computes them first.
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
-                  int32_t *sel, char *ws, const Workspace &wl, hipStream_t stream);
+                  int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
+                  hipStream_t stream);
 int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
                       float kv_scale, float sm_scale, uint16_t *out, char *ws,

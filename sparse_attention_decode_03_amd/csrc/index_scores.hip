@@ -17,6 +17,10 @@
 //    as M and 32 tokens as N; D is the reduction. A lane ends with 16 head
 //    partials of one token; ReLU, weight and head sum run in fp32 in a fixed
 //    order and one cross-lane add finishes the token (deterministic).
+//  - Optionally the pass also writes, for every row, the largest order key
+//    of each aligned 4-token and 32-token group (cross-lane max of the
+//    finished scores, two stores per 32 tokens). Selection draws its
+//    threshold from these.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -26,12 +30,12 @@ constexpr int kIdxThreads = 256; // 4 waves x 64 tokens of a tile
 
 // LDS: the key tile, 256 tokens x 16 chunks of 16 bytes (64 KiB at D = 128).
 
-template <int D, bool ONE_ROW>
+template <int D, bool ONE_ROW, bool GM>
 __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint16_t *__restrict__ k_normed, const int32_t *__restrict__ seq_lens,
-    float *__restrict__ scores, int K, int Hi, int64_t cap, int max_len, int stride,
-    int tiles_per_wg)
+    float *__restrict__ scores, uint32_t *__restrict__ gm4, uint32_t *__restrict__ gm32, int K,
+    int Hi, int64_t cap, int max_len, int stride, int tiles_per_wg)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per key row
     constexpr int KS = D / 16; // MFMA k-steps
@@ -142,43 +146,71 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                 const int t = t0 + wave * 64 + b * 32 + (lane & 31);
                 if (hl == 0 && t < L)
                     scores[(int64_t)r * stride + t] = tot;
+                if (GM) {
+                    // groups are aligned: lanes 4g..4g+3 and 0..31 of a half
+                    uint32_t k = t < L ? score_key(tot) : 0u;
+                    k = max(k, (uint32_t)__shfl_xor((int)k, 1, kWave));
+                    k = max(k, (uint32_t)__shfl_xor((int)k, 2, kWave));
+                    if (hl == 0 && (lane & 3) == 0 && t < L)
+                        gm4[(int64_t)r * (stride / 4) + (t >> 2)] = k;
+                    k = max(k, (uint32_t)__shfl_xor((int)k, 4, kWave));
+                    k = max(k, (uint32_t)__shfl_xor((int)k, 8, kWave));
+                    k = max(k, (uint32_t)__shfl_xor((int)k, 16, kWave));
+                    if (lane == 0 && t < L)
+                        gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k;
+                }
             }
         }
     }
 }
 
-template <int D, bool ONE_ROW>
+template <int D, bool ONE_ROW, bool GM>
 static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
-                       const uint16_t *k_normed, const int32_t *seq_lens, float *scores, int tpw,
-                       hipStream_t stream)
+                       const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
+                       uint32_t *gm4, uint32_t *gm32, int tpw, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_index_scores<D, ONE_ROW>), grid, dim3(kIdxThreads), 0, stream, q_idx, w,
-                       k_normed, seq_lens, scores, ls.rows_per_seq, ls.index_heads,
-                       (int64_t)ls.k_capacity, ls.max_len, score_stride(ls), tpw);
+    hipLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM>), grid, dim3(kIdxThreads), 0, stream,
+                       q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.rows_per_seq,
+                       ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls), tpw);
+}
+
+template <int D>
+static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
+                     const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
+                     uint32_t *gm4, uint32_t *gm32, int tpw, hipStream_t stream)
+{
+    const bool one = ls.rows_per_seq == 1;
+    const bool gm = gm4 != nullptr;
+    if (one && gm)
+        launch_one<D, true, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw,
+                                  stream);
+    else if (one)
+        launch_one<D, true, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw,
+                                   stream);
+    else if (gm)
+        launch_one<D, false, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
+                                   tpw, stream);
+    else
+        launch_one<D, false, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
+                                    tpw, stream);
 }
 
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                        hipStream_t stream)
+                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
 {
     // Each workgroup walks a run of tpw tiles of one sequence with the next
     // tile's loads in flight.
+    if ((gm4 == nullptr) != (gm32 == nullptr))
+        return -1;
     const int tpw = index_tiles_per_wg(ls);
     dim3 grid(index_wgs_per_seq(ls), ls.num_seqs);
-    const bool one = ls.rows_per_seq == 1;
-    if (ls.index_dim == 128) {
-        if (one)
-            launch_one<128, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, tpw, stream);
-        else
-            launch_one<128, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, tpw, stream);
-    } else if (ls.index_dim == 64) {
-        if (one)
-            launch_one<64, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, tpw, stream);
-        else
-            launch_one<64, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, tpw, stream);
-    } else {
+    if (ls.index_dim == 128)
+        launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw, stream);
+    else if (ls.index_dim == 64)
+        launch_d<64>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw, stream);
+    else
         return -1;
-    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -6,34 +6,54 @@
 // (pools of one token); -0.0 equals +0.0. Output: the selected ids in
 // ascending order, -1 past min(top_k, L_r).
 //
-// One workgroup of 1024 threads owns one row, so no step ever waits on
-// another workgroup. Radix selection on the order-preserving 32-bit key of
-// each score:
-//  1. sweep 1: a 2048-bin histogram of the key's top 11 bits (four LDS copies
-//     to spread atomic contention); the bin b* holding the k-th largest key
-//     follows from a suffix scan;
-//  2. sweep 2: keys above b* go straight into a bitmap of the row (one wave
-//     ballot builds eight bitmap words, no atomics); keys inside b* are the
-//     candidates, appended to LDS (or to a workspace spill past capacity);
-//  3. four radix passes over the candidates resolve the exact threshold key T
-//     and, among keys equal to T, the largest selected index;
-//  4. the selected candidates join the bitmap, and a block-wide scan of the
-//     bitmap's popcounts writes the ids in ascending order.
-// Sweeps read the row with 16-byte loads, two batches in flight.
+// Every comparison runs on the order-preserving 32-bit key of a score.
+//
+// Threshold. The index pass (or, for a standalone selection, a group-max
+// pass) leaves the largest key of each aligned 4-token and 32-token group.
+// Let tau be the k-th largest of a row's group keys: at least k distinct
+// tokens (the groups' maxima) have key >= tau, so the top-k of the row lies
+// inside {key >= tau}. For keys spread over the row, that set holds little
+// more than k tokens (about 1.4 k for 32-token groups at k = L / 64). This
+// holds for any input: the group keys only have to be keys of distinct
+// tokens of the row.
+//
+// Three steps, each a kernel boundary apart (no inter-workgroup waiting):
+//  1. filter (many workgroups per row, one 4096-token slice each): every
+//     workgroup finds tau by radix selection over the row's group keys
+//     (redundantly, so no workgroup waits on another), then writes the
+//     slice's keys >= tau, in ascending token order, to the slice's own
+//     candidate region;
+//  2. finish (one workgroup per row): gathers the candidates (already in
+//     ascending token order), radix-selects the exact k-th key T among them,
+//     and writes the tokens with key > T plus the lowest-index tokens with
+//     key == T, in ascending order;
+//  3. rows whose candidates do not fit the finishing workgroup (massive ties,
+//     adversarial orders, top_k beyond 2048 on mid-length rows) take a
+//     full-row radix selection in the same workgroup instead: slower, and
+//     exact in the same order.
+// Radix digits are taken relative to the block's key range (minimum key to
+// maximum key), so even a narrow score distribution spreads over the bins
+// and the LDS counters see little contention.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
 namespace dsa {
 
-constexpr int kRowThreads = 1024;
+constexpr int kSliceThreads = 256;          // filter workgroup
+constexpr int kSliceTokPerThread = kSelSlice / kSliceThreads; // 16
+constexpr int kGmRegs = 32;                 // group keys a filter thread keeps in registers
+constexpr int kFinThreads = 1024;           // finishing workgroup
+constexpr int kFinCap = 16384;              // candidates the finishing workgroup holds in LDS
+constexpr int kRowThreads = kFinThreads;    // full-row fallback runs in the same workgroup
 constexpr int kRowWaves = kRowThreads / kWave;
-constexpr int kVecBatch = 8;           // float4 loads per thread per batch
-constexpr int kCandCap = 6144;         // candidates kept in LDS (48 KiB)
-constexpr int kBitmapLdsWords = 12288; // rows up to 393216 tokens keep the bitmap in LDS
+constexpr int kVecBatch = 8;                // float4 loads per thread per batch (full row)
+constexpr int kCandCap = 6144;              // full-row candidates kept in LDS (48 KiB)
+constexpr int kBitmapLdsWords = 12288;      // full-row bitmap in LDS up to 393216 tokens
 
-// Shared state of one block-wide bin search.
+// Shared state of block-wide searches and reductions.
 struct BinSearch {
     uint32_t scan[kRowWaves + 1];
+    uint32_t red[2][kRowWaves];
     uint32_t bin;
     uint32_t before;
 };
@@ -41,12 +61,12 @@ struct BinSearch {
 // Over the LDS histogram h[0..nbins), walked from the highest bin down
 // (descending) or from bin 0 up (ascending), find the bin where the running
 // count first reaches `need` (1 <= need <= total). Returns the bin; *before is
-// the count of everything walked before it. All threads must call.
-template <bool Descending>
+// the count of everything walked before it. All NT threads must call.
+template <bool Descending, int NT>
 __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSearch *bs,
                              uint32_t *before)
 {
-    const int bpt = (nbins + kRowThreads - 1) / kRowThreads;
+    const int bpt = (nbins + NT - 1) / NT;
     const int tid = threadIdx.x;
     if (tid == 0) {
         bs->bin = 0u; // defined result even for an inconsistent histogram
@@ -59,7 +79,7 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
             local += h[Descending ? nbins - 1 - p : p];
     }
     uint32_t total;
-    uint32_t run = block_exclusive_scan<kRowThreads>(local, bs->scan, &total);
+    uint32_t run = block_exclusive_scan<NT>(local, bs->scan, &total);
     for (int i = 0; i < bpt; i++) {
         const int p = tid * bpt + i;
         if (p >= nbins)
@@ -79,45 +99,250 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
     return b;
 }
 
-// Spread the 8 bits of x to bit positions 0, 4, 8, ..., 28.
+// Block-wide minimum and maximum of one pair per thread.
+template <int NT>
+__device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
+{
+    constexpr int NW = NT / kWave;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, kWave));
+    }
+    const int wid = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        bs->red[0][wid] = lo;
+        bs->red[1][wid] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        lo = min(lo, bs->red[0][w]);
+        hi = max(hi, bs->red[1][w]);
+    }
+    __syncthreads();
+}
+
+// The rank-th largest key (1 <= rank <= number of keys) among the keys the
+// block's threads visit through for_keys(f) (f(key) once per key; each
+// thread visits its own share). Returns the key T; *above = number of keys
+// greater than T. Digits of up to 11 bits are taken relative to the minimum
+// key, from the top of the key range down, so at most three histogram passes
+// run. `hist` holds kHistBins LDS words. All NT threads must call.
+template <int NT, class ForKeys>
+__device__ uint32_t block_kth_largest(ForKeys for_keys, uint32_t rank, uint32_t *hist,
+                                      BinSearch *bs, uint32_t *above_out)
+{
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for_keys([&](uint32_t k) {
+        lo = min(lo, k);
+        hi = max(hi, k);
+    });
+    block_minmax<NT>(lo, hi, bs);
+    uint32_t base = lo;
+    int bits = hi > lo ? 32 - __clz(hi - lo) : 0; // hi - lo < 2^bits
+    uint32_t need = rank;
+    uint32_t above = 0;
+    while (bits > 0) {
+        const int shift = bits > 11 ? bits - 11 : 0;
+        const int nb = 1 << (bits - shift);
+        for (int i = threadIdx.x; i < nb; i += NT)
+            hist[i] = 0u;
+        __syncthreads();
+        // window [base, base + 2^bits): keys above it were counted before
+        for_keys([&](uint32_t k) {
+            const uint32_t d = (k - base) >> shift;
+            if (k >= base && d < (uint32_t)nb)
+                atomicAdd(&hist[d], 1u);
+        });
+        __syncthreads();
+        uint32_t bef;
+        const uint32_t b = find_bin<true, NT>(hist, nb, need, bs, &bef);
+        need -= bef;
+        above += bef;
+        base += b << shift;
+        bits = shift;
+    }
+    *above_out = above;
+    return base;
+}
+
+__device__ __forceinline__ int row_len(const int32_t *seq_lens, int r, int max_len)
+{
+    return min(max(seq_lens[r], 0), max_len);
+}
+
+// ---------------------------------------------------------------------------
+// Group maxima from a scores buffer (standalone selection only; the index
+// pass of a whole step writes the same arrays itself). Grid (slices, R).
+__global__ __launch_bounds__(kSliceThreads) void k_group_max(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
+    uint32_t *__restrict__ gm4, uint32_t *__restrict__ gm32, int max_len, int stride)
+{
+    const int r = blockIdx.y;
+    const int L = row_len(seq_lens, r, max_len);
+    const int s0 = blockIdx.x * kSelSlice;
+    if (s0 >= L)
+        return;
+    const int t0 = s0 + kSliceTokPerThread * threadIdx.x;
+    const float4 *row4 = (const float4 *)(scores + (int64_t)r * stride);
+    const int nvec = (L + 3) / 4;
+    uint32_t m4[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float4 v = row4[min(t0 / 4 + j, nvec - 1)];
+        const float e[4] = {v.x, v.y, v.z, v.w};
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            m = max(m, t0 + 4 * j + i < L ? score_key(e[i]) : 0u);
+        m4[j] = m;
+    }
+    uint32_t m16 = max(max(m4[0], m4[1]), max(m4[2], m4[3]));
+    const uint32_t m32 = max(m16, (uint32_t)__shfl_xor((int)m16, 1, kWave));
+    uint32_t *g4 = gm4 + (int64_t)r * (stride / 4);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        if (t0 + 4 * j < L)
+            g4[t0 / 4 + j] = m4[j];
+    if ((threadIdx.x & 1) == 0 && t0 < L)
+        gm32[(int64_t)r * (stride / 32) + t0 / 32] = m32;
+}
+
+// ---------------------------------------------------------------------------
+// Filter: grid (slices, R). Slice p of row r covers tokens
+// [4096 p, 4096 p + 4096) of [0, L); its candidates (key >= tau) go, in
+// ascending token order, to cand[r][4096 p ...], their number to cnt[r][p].
+__global__ __launch_bounds__(kSliceThreads) void k_select_filter(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
+    const uint32_t *__restrict__ gm4, const uint32_t *__restrict__ gm32,
+    u32x2 *__restrict__ cand, uint32_t *__restrict__ cnt, int max_len, int stride, int top_k,
+    int pmax)
+{
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ BinSearch bs;
+    const int r = blockIdx.y;
+    const int p = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = row_len(seq_lens, r, max_len);
+    const int s0 = p * kSelSlice;
+    if (L <= top_k || s0 >= L)
+        return;
+
+    // this slice's scores: issued first, they land while tau is found
+    const int t0 = s0 + kSliceTokPerThread * tid;
+    const float4 *row4 = (const float4 *)(scores + (int64_t)r * stride);
+    const int nvec = (L + 3) / 4;
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        v[j] = row4[min(t0 / 4 + j, nvec - 1)];
+
+    // tau from the finest group level that still has at least top_k groups
+    // and whose keys fit the registers; failing both, every token is a
+    // candidate (then L < 4 top_k)
+    const int ng32 = (L + 31) / 32;
+    const int ng4 = (L + 3) / 4;
+    const uint32_t *gm = nullptr;
+    int ng = 0;
+    if (ng4 >= top_k && ng4 <= kGmRegs * kSliceThreads) {
+        gm = gm4 + (int64_t)r * (stride / 4);
+        ng = ng4;
+    } else if (ng32 >= top_k) {
+        gm = gm32 + (int64_t)r * (stride / 32);
+        ng = ng32;
+    } else if (ng4 >= top_k) {
+        gm = gm4 + (int64_t)r * (stride / 4);
+        ng = ng4;
+    }
+    uint32_t tau = 0u;
+    if (gm != nullptr) {
+        uint32_t above;
+        if (ng <= kGmRegs * kSliceThreads) {
+            const int nj = (ng + kSliceThreads - 1) / kSliceThreads;
+            uint32_t kk[kGmRegs];
+#pragma unroll
+            for (int j = 0; j < kGmRegs; j++)
+                kk[j] = gm[min(tid + kSliceThreads * j, ng - 1)];
+            tau = block_kth_largest<kSliceThreads>(
+                [&](auto &&f) {
+#pragma unroll
+                    for (int j = 0; j < kGmRegs; j++)
+                        if (j < nj && tid + kSliceThreads * j < ng)
+                            f(kk[j]);
+                },
+                (uint32_t)top_k, hist, &bs, &above);
+        } else {
+            tau = block_kth_largest<kSliceThreads>(
+                [&](auto &&f) {
+                    for (int i = tid; i < ng; i += kSliceThreads)
+                        f(gm[i]);
+                },
+                (uint32_t)top_k, hist, &bs, &above);
+        }
+    }
+
+    uint32_t key[kSliceTokPerThread];
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = t0 + 4 * j + i;
+            key[4 * j + i] = score_key(e[i]);
+            c += (t < L && key[4 * j + i] >= tau) ? 1u : 0u;
+        }
+    }
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan<kSliceThreads>(c, bs.scan, &total);
+    u32x2 *dst = cand + (int64_t)r * stride + s0;
+#pragma unroll
+    for (int i = 0; i < kSliceTokPerThread; i++) {
+        const int t = t0 + i;
+        if (t < L && key[i] >= tau)
+            dst[pos++] = u32x2{key[i], (uint32_t)t};
+    }
+    if (tid == 0)
+        cnt[(int64_t)r * pmax + p] = total;
+}
+
+// ---------------------------------------------------------------------------
+// Full-row radix selection (fallback of the finishing workgroup). LDS comes
+// from the caller: hsub [4][kHistBins], cbuf [kCandCap], lbitmap
+// [kBitmapLdsWords].
+//  1. sweep 1: histogram of the key's top 11 bits (four LDS copies to spread
+//     contention); the bin b* holding the k-th largest key follows;
+//  2. sweep 2: keys above b* go straight into a bitmap of the row (one wave
+//     ballot builds eight bitmap words); keys inside b* are appended to LDS
+//     (or to the workspace past capacity);
+//  3. four radix passes over those resolve the exact threshold key T and,
+//     among keys equal to T, the largest selected index;
+//  4. the selected ones join the bitmap; a block-wide scan of its popcounts
+//     writes the ids in ascending order.
 __device__ __forceinline__ uint32_t spread8(uint32_t x)
 {
+    // the 8 bits of x to bit positions 0, 4, 8, ..., 28
     x = (x | (x << 12)) & 0x000F000Fu;
     x = (x | (x << 6)) & 0x03030303u;
     x = (x | (x << 3)) & 0x11111111u;
     return x;
 }
 
-__global__ __launch_bounds__(kRowThreads) void k_select_row(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
-    int32_t *__restrict__ sel, u32x2 *__restrict__ spill, uint32_t *__restrict__ gbitmap,
-    int max_len, int stride, int top_k)
+__device__ void select_row_full(const float *__restrict__ scores, int r, int L, int32_t *out,
+                                u32x2 *rspill, uint32_t *gbitmap_row, int stride, int top_k,
+                                uint32_t (*hsub)[kHistBins], u32x2 *cbuf, uint32_t *lbitmap,
+                                BinSearch *bs, uint32_t *ccount)
 {
-    __shared__ uint32_t hsub[4][kHistBins];
-    __shared__ u32x2 cbuf[kCandCap];
-    __shared__ uint32_t lbitmap[kBitmapLdsWords];
-    __shared__ BinSearch bs;
-    __shared__ uint32_t ccount;
-
-    const int r = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
-    const int L = min(max(seq_lens[r], 0), max_len);
-    int32_t *out = sel + (int64_t)r * top_k;
-
-    if (L <= top_k) { // every token is selected; slots past L are padding
-        for (int slot = tid; slot < top_k; slot += kRowThreads)
-            out[slot] = slot < L ? slot : -1;
-        return;
-    }
-
     const float4 *row4 = (const float4 *)(scores + (int64_t)r * stride);
     const int nvec = (L + 3) / 4; // float4s covering [0, L) (all inside the row stride)
     constexpr int kBatchTok = kRowThreads * kVecBatch * 4;
     // Two batches of kVecBatch float4 per thread in flight; f(t, v) runs for
-    // the float4 v holding tokens t .. t+3 (t a multiple of 4; entries at or
-    // past L are masked by f).
+    // the float4 v holding tokens t .. t+3 (entries at or past L are masked
+    // by f).
     auto sweep = [&](auto &&f) {
         float4 a[kVecBatch], b[kVecBatch];
         auto load = [&](float4(&x)[kVecBatch], int base) {
@@ -153,22 +378,22 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
 #pragma unroll
         for (int j = 0; j < 4; j++)
             if (t + j < L)
-                atomicAdd(&myh[score_key(e[j]) >> kHistShift], 1u);
+                atomicAdd(&myh[score_key(e[j]) >> 21], 1u);
     });
     __syncthreads();
     for (int i = tid; i < kHistBins; i += kRowThreads)
         hsub[0][i] += hsub[1][i] + hsub[2][i] + hsub[3][i];
     if (tid == 0)
-        ccount = 0u;
+        *ccount = 0u;
     __syncthreads();
     uint32_t above;
-    const uint32_t bstar = find_bin<true>(hsub[0], kHistBins, (uint32_t)top_k, &bs, &above);
+    const uint32_t bstar =
+        find_bin<true, kRowThreads>(hsub[0], kHistBins, (uint32_t)top_k, bs, &above);
     const uint32_t need = (uint32_t)top_k - above; // keys to take from bin b*
 
     // ---- sweep 2: keys above b* -> bitmap; keys inside b* -> candidates ----
     const int nwords = (L + 31) / 32;
-    uint32_t *bm = nwords <= kBitmapLdsWords ? lbitmap : gbitmap + (int64_t)r * (stride / 32);
-    u32x2 *rspill = spill + (int64_t)r * stride;
+    uint32_t *bm = nwords <= kBitmapLdsWords ? lbitmap : gbitmap_row;
     sweep([&](int t, float4 v) {
         const float e[4] = {v.x, v.y, v.z, v.w};
         uint64_t ab[4];
@@ -176,7 +401,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
         for (int j = 0; j < 4; j++) {
             const bool valid = t + j < L;
             const uint32_t key = score_key(e[j]);
-            const uint32_t bin = key >> kHistShift;
+            const uint32_t bin = key >> 21;
             ab[j] = __ballot(valid && bin > bstar);
             const bool in = valid && bin == bstar;
             const uint64_t cm = __ballot(in);
@@ -184,7 +409,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
                 const int leader = __ffsll((unsigned long long)cm) - 1;
                 uint32_t pos = 0;
                 if (lane == leader)
-                    pos = atomicAdd(&ccount, (uint32_t)__popcll(cm));
+                    pos = atomicAdd(ccount, (uint32_t)__popcll(cm));
                 pos = __shfl(pos, leader, kWave);
                 if (in) {
                     const uint32_t at = pos + (uint32_t)__popcll(cm & ((1ull << lane) - 1ull));
@@ -209,7 +434,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
         }
     });
     __syncthreads();
-    const uint32_t m = min(ccount, (uint32_t)L);
+    const uint32_t m = min(*ccount, (uint32_t)L);
     auto cand_at = [&](uint32_t i) -> u32x2 { return i < (uint32_t)kCandCap ? cbuf[i] : rspill[i]; };
 
     // ---- radix passes over the candidates ----
@@ -225,7 +450,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
         atomicAdd(&h[(cand_at(i).x >> 10) & 0x7FFu], 1u);
     __syncthreads();
     uint32_t bef;
-    const uint32_t a_bin = find_bin<true>(h, 2048, need, &bs, &bef);
+    const uint32_t a_bin = find_bin<true, kRowThreads>(h, 2048, need, bs, &bef);
     const uint32_t need_a = need - bef;
     const uint32_t hi21 = (bstar << 11) | a_bin; // key >> 10
     // pass B: key bits [9:0] among key >> 10 == hi21, descending
@@ -236,7 +461,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
             atomicAdd(&h[k & 0x3FFu], 1u);
     }
     __syncthreads();
-    const uint32_t b_bin = find_bin<true>(h, 1024, need_a, &bs, &bef);
+    const uint32_t b_bin = find_bin<true, kRowThreads>(h, 1024, need_a, bs, &bef);
     const uint32_t need_t = need_a - bef; // keys equal to T to take
     const uint32_t eq_count = h[b_bin];
     const uint32_t T = (hi21 << 10) | b_bin;
@@ -251,7 +476,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
                 atomicAdd(&h[(e.y >> 11) & 0x7FFu], 1u);
         }
         __syncthreads();
-        const uint32_t c_bin = find_bin<false>(h, 2048, need_t, &bs, &bef);
+        const uint32_t c_bin = find_bin<false, kRowThreads>(h, 2048, need_t, bs, &bef);
         const uint32_t need_c = need_t - bef;
         // pass D: index bits [10:0] among keys == T in index block c_bin
         clear_h();
@@ -261,7 +486,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
                 atomicAdd(&h[e.y & 0x7FFu], 1u);
         }
         __syncthreads();
-        const uint32_t d_bin = find_bin<false>(h, 2048, need_c, &bs, &bef);
+        const uint32_t d_bin = find_bin<false, kRowThreads>(h, 2048, need_c, bs, &bef);
         cut = (int32_t)((c_bin << 11) | d_bin);
     }
 
@@ -281,7 +506,7 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
         if (w0 + i < nwords)
             cnt += __popc(bm[w0 + i]);
     uint32_t total;
-    uint32_t pos = block_exclusive_scan<kRowThreads>(cnt, bs.scan, &total);
+    uint32_t pos = block_exclusive_scan<kRowThreads>(cnt, bs->scan, &total);
     for (int i = 0; i < wpt; i++) {
         if (w0 + i >= nwords)
             break;
@@ -294,12 +519,133 @@ __global__ __launch_bounds__(kRowThreads) void k_select_row(
     }
 }
 
-int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
-                  int32_t *sel, char *ws, const Workspace &wl, hipStream_t stream)
+// ---------------------------------------------------------------------------
+// Finish: one workgroup per row.
+constexpr int kFinLdsBytes = kFinCap * 8;  // candidates; the full-row path reuses it
+static_assert(4 * kHistBins * 4 + kCandCap * 8 + kBitmapLdsWords * 4 <= kFinLdsBytes,
+              "full-row LDS must fit the candidate area");
+
+__global__ __launch_bounds__(kFinThreads) void k_select_finish(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
+    u32x2 *__restrict__ cand, const uint32_t *__restrict__ cnt, int32_t *__restrict__ sel,
+    uint32_t *__restrict__ gbitmap, int max_len, int stride, int top_k, int pmax)
 {
-    hipLaunchKernelGGL(k_select_row, dim3(ls.num_rows), dim3(kRowThreads), 0, stream, scores,
-                       seq_lens, sel, (u32x2 *)(ws + wl.spill), (uint32_t *)(ws + wl.bitmap),
-                       ls.max_len, score_stride(ls), ls.top_k);
+    __shared__ __align__(16) uint8_t area[kFinLdsBytes];
+    __shared__ uint32_t pre[kFinThreads];
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ BinSearch bs;
+    __shared__ uint32_t ccount;
+
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = row_len(seq_lens, r, max_len);
+    int32_t *out = sel + (int64_t)r * top_k;
+
+    if (L <= top_k) { // every token is selected; slots past L are padding
+        for (int slot = tid; slot < top_k; slot += kFinThreads)
+            out[slot] = slot < L ? slot : -1;
+        return;
+    }
+
+    // candidate counts of the row's slices -> offsets
+    const int P = (L + kSelSlice - 1) / kSelSlice; // <= pmax <= kFinThreads
+    const uint32_t c = tid < P ? cnt[(int64_t)r * pmax + tid] : 0u;
+    uint32_t m;
+    const uint32_t off = block_exclusive_scan<kFinThreads>(c, bs.scan, &m);
+    if (tid < P)
+        pre[tid] = off;
+    __syncthreads();
+
+    const u32x2 *src = cand + (int64_t)r * stride;
+    if (m < (uint32_t)top_k || m > (uint32_t)kFinCap) {
+        uint32_t(*hsub)[kHistBins] = (uint32_t(*)[kHistBins])area;
+        u32x2 *cbuf = (u32x2 *)(area + 4 * kHistBins * 4);
+        uint32_t *lbitmap = (uint32_t *)(area + 4 * kHistBins * 4 + kCandCap * 8);
+        select_row_full(scores, r, L, out, cand + (int64_t)r * stride,
+                        gbitmap + (int64_t)r * (stride / 32), stride, top_k, hsub, cbuf, lbitmap,
+                        &bs, &ccount);
+        return;
+    }
+
+    // gather the candidates (slice order = ascending token order), four
+    // loads in flight per thread
+    u32x2 *cl = (u32x2 *)area;
+    for (int i0 = 0; i0 < (int)m; i0 += 4 * kFinThreads) {
+        u32x2 e[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int i = min(i0 + j * kFinThreads + tid, (int)m - 1);
+            int lo = 0, hi = P - 1; // last slice whose offset is <= i
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pre[mid] <= (uint32_t)i)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            e[j] = src[(int64_t)lo * kSelSlice + (i - (int)pre[lo])];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int i = i0 + j * kFinThreads + tid;
+            if (i < (int)m)
+                cl[i] = e[j];
+        }
+    }
+    __syncthreads();
+
+    uint32_t above;
+    const uint32_t T = block_kth_largest<kFinThreads>(
+        [&](auto &&f) {
+            for (int i = tid; i < (int)m; i += kFinThreads)
+                f(cl[i].x);
+        },
+        (uint32_t)top_k, hist, &bs, &above);
+    const uint32_t need_eq = (uint32_t)top_k - above; // keys == T to take, lowest index first
+
+    // each thread a contiguous run of candidates; one scan of the packed
+    // (equal, greater) counts places every selected id
+    const int run = ((int)m + kFinThreads - 1) / kFinThreads;
+    const int i0 = min(tid * run, (int)m);
+    const int i1 = min(i0 + run, (int)m);
+    uint32_t ngt = 0, neq = 0;
+    for (int i = i0; i < i1; i++) {
+        const uint32_t k = cl[i].x;
+        ngt += k > T ? 1u : 0u;
+        neq += k == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pk = block_exclusive_scan<kFinThreads>((neq << 16) | ngt, bs.scan, &tot);
+    uint32_t eqi = pk >> 16;
+    uint32_t pos = (pk & 0xFFFFu) + min(eqi, need_eq);
+    for (int i = i0; i < i1; i++) {
+        const u32x2 e = cl[i];
+        const bool take = e.x > T || (e.x == T && eqi < need_eq);
+        eqi += e.x == T ? 1u : 0u;
+        if (take && pos < (uint32_t)top_k)
+            out[pos++] = (int32_t)e.y;
+    }
+}
+
+int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
+                  int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
+                  hipStream_t stream)
+{
+    const int pmax = sel_slices(ls);
+    const int stride = score_stride(ls);
+    uint32_t *gm4 = (uint32_t *)(ws + wl.gm4);
+    uint32_t *gm32 = (uint32_t *)(ws + wl.gm32);
+    u32x2 *cand = (u32x2 *)(ws + wl.cand);
+    uint32_t *cnt = (uint32_t *)(ws + wl.cnt);
+    const dim3 slices(pmax, ls.num_rows);
+    if (!have_group_max)
+        hipLaunchKernelGGL(k_group_max, slices, dim3(kSliceThreads), 0, stream, scores, seq_lens,
+                           gm4, gm32, ls.max_len, stride);
+    hipLaunchKernelGGL(k_select_filter, slices, dim3(kSliceThreads), 0, stream, scores, seq_lens,
+                       gm4, gm32, cand, cnt, ls.max_len, stride, ls.top_k, pmax);
+    hipLaunchKernelGGL(k_select_finish, dim3(ls.num_rows), dim3(kFinThreads), 0, stream, scores,
+                       seq_lens, cand, cnt, sel, (uint32_t *)(ws + wl.bitmap), ls.max_len, stride,
+                       ls.top_k, pmax);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
