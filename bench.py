@@ -148,7 +148,9 @@ def main() -> int:
         warm = time.perf_counter() - wt0
 
         # dominant kernel: the index-score pass, timed per launch with HIP
-        # events recorded on the stream it runs on
+        # events recorded on the stream it runs on, inside step-shaped
+        # iterations (index, select, attend through the stage entry points,
+        # rotating replicas as the timed steps do)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.index_launches)]
         for i, (a, b) in enumerate(evs):
@@ -156,6 +158,10 @@ def main() -> int:
             dsa.index_scores(sh, step.q_idx, step.w, keys[i % nrep], step.seq_lens, step.scores,
                              stream=stream)
             b.record(stream)
+            dsa.topk_select(sh, step.scores, step.seq_lens, step.sel, step.ws, stream=stream)
+            dsa.mla_decode(sh, step.q, pools[i % nrep], step.block_tables, step.seq_lens,
+                           step.sel, step.kv_scale, step.sm_scale, step.out, step.ws,
+                           stream=stream)
         torch.cuda.synchronize()
         idx_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 

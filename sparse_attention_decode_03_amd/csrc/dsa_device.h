@@ -84,6 +84,19 @@ __device__ __forceinline__ uint32_t score_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Data-parallel lane moves (VALU, no LDS round trip). Controls: quad
+// permutations xor 1 and xor 2, mirror inside each half-row of 8 lanes and
+// inside each row of 16 lanes.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
 // Block-wide exclusive prefix sum of one value per thread (blockDim.x == NT).
 // `scratch` holds NT/64 + 1 words of LDS. Returns the exclusive prefix; the
 // block total lands in *total.

@@ -7,7 +7,7 @@
 // cache is read token-major as k[raw * D + d]).
 //
 // Design (HBM-bound: 256 B of keys per token at D = 128 against 8 kflop):
-//  - One workgroup walks a run of 256-token tiles of one sequence and scores
+//  - One workgroup walks every W-th 256-token tile of one sequence and scores
 //    each tile for every row of that sequence (the K rows of a verify share
 //    one key read). Keys stream HBM -> VGPR with fully coalesced 16-byte
 //    loads (the next tile's loads are in flight while the current tile
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint16_t *__restrict__ k_normed, const int32_t *__restrict__ seq_lens,
     float *__restrict__ scores, uint32_t *__restrict__ gm4, uint32_t *__restrict__ gm32, int K,
-    int Hi, int64_t cap, int max_len, int stride, int tiles_per_wg)
+    int Hi, int64_t cap, int max_len, int stride)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per key row
     constexpr int KS = D / 16; // MFMA k-steps
@@ -51,8 +51,12 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     int lmax = 0;
     for (int j = 0; j < K; j++)
         lmax = max(lmax, min(max(seq_lens[s * K + j], 0), max_len));
-    const int tile_first = blockIdx.x * tiles_per_wg;
-    const int tile_end = min(tile_first + tiles_per_wg, (lmax + kIdxTile - 1) / kIdxTile);
+    // tiles interleave across the sequence's workgroups (workgroup x takes
+    // tiles x, x + W, x + 2W, ...), so at any moment the workgroups stream
+    // neighbouring 64 KiB blocks and spread over every HBM channel
+    const int W = gridDim.x;
+    const int tile_first = blockIdx.x;
+    const int tile_end = (lmax + kIdxTile - 1) / kIdxTile;
     if (tile_first >= tile_end)
         return;
 
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         load_row(s);
 
     load_tile(tile_first);
-    for (int tile = tile_first; tile < tile_end; tile++) {
+    for (int tile = tile_first; tile < tile_end; tile += W) {
         const int t0 = tile * kIdxTile;
         __syncthreads(); // every wave is done reading the previous tile
 #pragma unroll
@@ -110,8 +114,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
             lds[row * CH + (c ^ (row & (CH - 1)))] = regs[i];
         }
         __syncthreads();
-        if (tile + 1 < tile_end)
-            load_tile(tile + 1); // in flight while this tile computes
+        if (tile + W < tile_end)
+            load_tile(tile + W); // in flight while this tile computes
 
         // key operands: column (token) lane%32, k-chunks hl*KS + ks
         bf16x8 kb[2][KS];
@@ -147,17 +151,19 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                 if (hl == 0 && t < L)
                     scores[(int64_t)r * stride + t] = tot;
                 if (GM) {
-                    // groups are aligned: lanes 4g..4g+3 and 0..31 of a half
+                    // groups are aligned: a quad of lanes holds a 4-token
+                    // group, lanes 0..31 the 32-token group
                     uint32_t k = t < L ? score_key(tot) : 0u;
-                    k = max(k, (uint32_t)__shfl_xor((int)k, 1, kWave));
-                    k = max(k, (uint32_t)__shfl_xor((int)k, 2, kWave));
+                    k = max(k, dpp_u32<kDppQuadXor1>(k));
+                    k = max(k, dpp_u32<kDppQuadXor2>(k));
                     if (hl == 0 && (lane & 3) == 0 && t < L)
                         gm4[(int64_t)r * (stride / 4) + (t >> 2)] = k;
-                    k = max(k, (uint32_t)__shfl_xor((int)k, 4, kWave));
-                    k = max(k, (uint32_t)__shfl_xor((int)k, 8, kWave));
-                    k = max(k, (uint32_t)__shfl_xor((int)k, 16, kWave));
+                    k = max(k, dpp_u32<kDppRowHalfMirror>(k));
+                    k = max(k, dpp_u32<kDppRowMirror>(k)); // every lane: its row's max
+                    const uint32_t k32 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 0),
+                                             (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
                     if (lane == 0 && t < L)
-                        gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k;
+                        gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k32;
                 }
             }
         }
@@ -167,48 +173,47 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 template <int D, bool ONE_ROW, bool GM>
 static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
                        const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                       uint32_t *gm4, uint32_t *gm32, int tpw, hipStream_t stream)
+                       uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
 {
     hipLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM>), grid, dim3(kIdxThreads), 0, stream,
                        q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.rows_per_seq,
-                       ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls), tpw);
+                       ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls));
 }
 
 template <int D>
 static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
                      const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                     uint32_t *gm4, uint32_t *gm32, int tpw, hipStream_t stream)
+                     uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
 {
     const bool one = ls.rows_per_seq == 1;
     const bool gm = gm4 != nullptr;
     if (one && gm)
-        launch_one<D, true, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw,
+        launch_one<D, true, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                   stream);
     else if (one)
-        launch_one<D, true, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw,
+        launch_one<D, true, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                    stream);
     else if (gm)
         launch_one<D, false, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
-                                   tpw, stream);
+                                   stream);
     else
         launch_one<D, false, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
-                                    tpw, stream);
+                                    stream);
 }
 
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
                         uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
 {
-    // Each workgroup walks a run of tpw tiles of one sequence with the next
-    // tile's loads in flight.
+    // About 512 workgroups in all; each walks every W-th tile of one
+    // sequence with the next tile's loads in flight.
     if ((gm4 == nullptr) != (gm32 == nullptr))
         return -1;
-    const int tpw = index_tiles_per_wg(ls);
     dim3 grid(index_wgs_per_seq(ls), ls.num_seqs);
     if (ls.index_dim == 128)
-        launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw, stream);
+        launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream);
     else if (ls.index_dim == 64)
-        launch_d<64>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, tpw, stream);
+        launch_d<64>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream);
     else
         return -1;
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -43,7 +43,7 @@ constexpr int kSliceThreads = 256;          // filter workgroup
 constexpr int kSliceTokPerThread = kSelSlice / kSliceThreads; // 16
 constexpr int kGmRegs = 32;                 // group keys a filter thread keeps in registers
 constexpr int kFinThreads = 1024;           // finishing workgroup
-constexpr int kFinCap = 16384;              // candidates the finishing workgroup holds in LDS
+constexpr int kFinCap = 16384;              // candidates the finishing workgroup holds
 constexpr int kRowThreads = kFinThreads;    // full-row fallback runs in the same workgroup
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kVecBatch = 8;                // float4 loads per thread per batch (full row)
@@ -123,47 +123,116 @@ __device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
     __syncthreads();
 }
 
-// The rank-th largest key (1 <= rank <= number of keys) among the keys the
-// block's threads visit through for_keys(f) (f(key) once per key; each
-// thread visits its own share). Returns the key T; *above = number of keys
-// greater than T. Digits of up to 11 bits are taken relative to the minimum
-// key, from the top of the key range down, so at most three histogram passes
-// run. `hist` holds kHistBins LDS words. All NT threads must call.
+// Descending walk over the kHistBins-bin LDS histogram h (16-byte aligned):
+// the bin where the running count first reaches `need`, and the count of
+// everything above it, into bs. Run by wave 0 alone (32 bins per lane, one
+// lane scan); a barrier of the caller publishes the result. An inconsistent
+// histogram (total < need) yields bin 0.
+__device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t need,
+                                                    BinSearch *bs)
+{
+    constexpr int BPL = kHistBins / kWave; // 32
+    const int lane = threadIdx.x;
+    const int lo_b = kHistBins - BPL * (lane + 1); // lane 0 holds the top bins
+    uint32_t c[BPL];
+#pragma unroll
+    for (int q = 0; q < BPL / 4; q++) {
+        const u32x4 v = *(const u32x4 *)(h + lo_b + 4 * q);
+        c[4 * q] = v.x;
+        c[4 * q + 1] = v.y;
+        c[4 * q + 2] = v.z;
+        c[4 * q + 3] = v.w;
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < BPL; i++)
+        local += c[i];
+    uint32_t x = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, o, kWave);
+        if (lane >= o)
+            x += y;
+    }
+    const uint32_t run = x - local; // count in the bins of lower lanes (higher bins)
+    if (lane == 0) {
+        bs->bin = 0u;
+        bs->before = 0u;
+    }
+    if (run < need && x >= need) { // exactly one lane
+        uint32_t bef = run;
+        uint32_t bin = (uint32_t)lo_b;
+        bool found = false;
+#pragma unroll
+        for (int i = BPL - 1; i >= 0; i--) {
+            if (!found) {
+                if (bef + c[i] >= need) {
+                    bin = (uint32_t)(lo_b + i);
+                    found = true;
+                } else {
+                    bef += c[i];
+                }
+            }
+        }
+        bs->bin = bin;
+        bs->before = bef;
+    }
+}
+
+// Radix selection of the rank-th largest key (1 <= rank <= number of keys)
+// among the keys the block's threads visit through for_keys(f) (f(key) once
+// per key; each thread visits its own share). Digits of up to 11 bits are
+// taken relative to the block's minimum key, from the top of the key range
+// down; `hist` is two LDS histograms (one counts while the other is cleared),
+// so a pass costs two barriers. After at most max_passes passes, returns the
+// lower end of the remaining key window: every key >= it is counted, at
+// least `rank` keys are >= it, and no key >= it is below the rank-th largest
+// key's window. *exact tells whether the window shrank to the single key T =
+// the rank-th largest (always so for max_passes >= 3); then *above counts
+// the keys greater than T. All NT threads must call.
 template <int NT, class ForKeys>
-__device__ uint32_t block_kth_largest(ForKeys for_keys, uint32_t rank, uint32_t *hist,
-                                      BinSearch *bs, uint32_t *above_out)
+__device__ uint32_t block_kth_largest(ForKeys for_keys, uint32_t rank,
+                                      uint32_t (*hist)[kHistBins], BinSearch *bs, int max_passes,
+                                      uint32_t *above_out, bool *exact)
 {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for_keys([&](uint32_t k) {
         lo = min(lo, k);
         hi = max(hi, k);
     });
-    block_minmax<NT>(lo, hi, bs);
+    for (int i = threadIdx.x; i < kHistBins; i += NT)
+        hist[0][i] = 0u;
+    block_minmax<NT>(lo, hi, bs); // its barriers also publish the cleared hist[0]
     uint32_t base = lo;
     int bits = hi > lo ? 32 - __clz(hi - lo) : 0; // hi - lo < 2^bits
     uint32_t need = rank;
     uint32_t above = 0;
-    while (bits > 0) {
+    for (int pass = 0; bits > 0 && pass < max_passes; pass++) {
+        uint32_t *h = hist[pass & 1];
         const int shift = bits > 11 ? bits - 11 : 0;
-        const int nb = 1 << (bits - shift);
-        for (int i = threadIdx.x; i < nb; i += NT)
-            hist[i] = 0u;
-        __syncthreads();
+        const uint32_t nb = 1u << (bits - shift);
         // window [base, base + 2^bits): keys above it were counted before
         for_keys([&](uint32_t k) {
             const uint32_t d = (k - base) >> shift;
-            if (k >= base && d < (uint32_t)nb)
-                atomicAdd(&hist[d], 1u);
+            if (k >= base && d < nb)
+                atomicAdd(&h[d], 1u);
         });
         __syncthreads();
-        uint32_t bef;
-        const uint32_t b = find_bin<true, NT>(hist, nb, need, bs, &bef);
+        uint32_t *other = hist[(pass + 1) & 1];
+        for (int i = threadIdx.x; i < kHistBins; i += NT)
+            other[i] = 0u;
+        if (threadIdx.x < kWave)
+            find_bin_desc_wave0(h, need, bs);
+        __syncthreads();
+        const uint32_t b = bs->bin;
+        const uint32_t bef = bs->before;
         need -= bef;
         above += bef;
         base += b << shift;
         bits = shift;
     }
     *above_out = above;
+    *exact = bits == 0;
     return base;
 }
 
@@ -219,7 +288,7 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
     u32x2 *__restrict__ cand, uint32_t *__restrict__ cnt, int max_len, int stride, int top_k,
     int pmax)
 {
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ __align__(16) uint32_t hist[2][kHistBins];
     __shared__ BinSearch bs;
     const int r = blockIdx.y;
     const int p = blockIdx.x;
@@ -255,9 +324,12 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
         gm = gm4 + (int64_t)r * (stride / 4);
         ng = ng4;
     }
+    // two digit passes leave a window of at most 2^10 keys; its lower end
+    // is a valid threshold (at least top_k group keys are >= it)
     uint32_t tau = 0u;
     if (gm != nullptr) {
         uint32_t above;
+        bool exact;
         if (ng <= kGmRegs * kSliceThreads) {
             const int nj = (ng + kSliceThreads - 1) / kSliceThreads;
             uint32_t kk[kGmRegs];
@@ -271,14 +343,14 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
                         if (j < nj && tid + kSliceThreads * j < ng)
                             f(kk[j]);
                 },
-                (uint32_t)top_k, hist, &bs, &above);
+                (uint32_t)top_k, hist, &bs, 2, &above, &exact);
         } else {
             tau = block_kth_largest<kSliceThreads>(
                 [&](auto &&f) {
                     for (int i = tid; i < ng; i += kSliceThreads)
                         f(gm[i]);
                 },
-                (uint32_t)top_k, hist, &bs, &above);
+                (uint32_t)top_k, hist, &bs, 2, &above, &exact);
         }
     }
 
@@ -520,19 +592,20 @@ __device__ void select_row_full(const float *__restrict__ scores, int r, int L, 
 }
 
 // ---------------------------------------------------------------------------
-// Finish: one workgroup per row.
-constexpr int kFinLdsBytes = kFinCap * 8;  // candidates; the full-row path reuses it
-static_assert(4 * kHistBins * 4 + kCandCap * 8 + kBitmapLdsWords * 4 <= kFinLdsBytes,
-              "full-row LDS must fit the candidate area");
+// Finish: one workgroup per row. Thread t owns the contiguous run of
+// candidates [t * run, t * run + run) in registers (run <= 16), so the
+// selected ids leave in ascending order straight from registers.
+constexpr int kFinRun = kFinCap / kFinThreads; // 16
+constexpr int kFullLdsBytes = 4 * kHistBins * 4 + kCandCap * 8 + kBitmapLdsWords * 4;
 
 __global__ __launch_bounds__(kFinThreads) void k_select_finish(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
     u32x2 *__restrict__ cand, const uint32_t *__restrict__ cnt, int32_t *__restrict__ sel,
     uint32_t *__restrict__ gbitmap, int max_len, int stride, int top_k, int pmax)
 {
-    __shared__ __align__(16) uint8_t area[kFinLdsBytes];
+    __shared__ __align__(16) uint8_t area[kFullLdsBytes]; // full-row fallback only
     __shared__ uint32_t pre[kFinThreads];
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ __align__(16) uint32_t hist[2][kHistBins];
     __shared__ BinSearch bs;
     __shared__ uint32_t ccount;
 
@@ -550,14 +623,14 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
     // candidate counts of the row's slices -> offsets
     const int P = (L + kSelSlice - 1) / kSelSlice; // <= pmax <= kFinThreads
     const uint32_t c = tid < P ? cnt[(int64_t)r * pmax + tid] : 0u;
-    uint32_t m;
-    const uint32_t off = block_exclusive_scan<kFinThreads>(c, bs.scan, &m);
+    uint32_t mu;
+    const uint32_t off = block_exclusive_scan<kFinThreads>(c, bs.scan, &mu);
     if (tid < P)
         pre[tid] = off;
     __syncthreads();
+    const int m = (int)mu;
 
-    const u32x2 *src = cand + (int64_t)r * stride;
-    if (m < (uint32_t)top_k || m > (uint32_t)kFinCap) {
+    if (m < top_k || m > kFinCap) {
         uint32_t(*hsub)[kHistBins] = (uint32_t(*)[kHistBins])area;
         u32x2 *cbuf = (u32x2 *)(area + 4 * kHistBins * 4);
         uint32_t *lbitmap = (uint32_t *)(area + 4 * kHistBins * 4 + kCandCap * 8);
@@ -567,63 +640,74 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         return;
     }
 
-    // gather the candidates (slice order = ascending token order), four
-    // loads in flight per thread
-    u32x2 *cl = (u32x2 *)area;
-    for (int i0 = 0; i0 < (int)m; i0 += 4 * kFinThreads) {
-        u32x2 e[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int i = min(i0 + j * kFinThreads + tid, (int)m - 1);
-            int lo = 0, hi = P - 1; // last slice whose offset is <= i
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (pre[mid] <= (uint32_t)i)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            e[j] = src[(int64_t)lo * kSelSlice + (i - (int)pre[lo])];
+    // this thread's run, gathered from the slices' regions (all loads in
+    // flight at once; indices past the run repeat the last candidate)
+    const int run = (m + kFinThreads - 1) / kFinThreads;
+    const int i0 = min(tid * run, m);
+    const int n_own = min(run, m - i0);
+    int sl = 0; // slice of candidate min(i0, m - 1): last offset <= it
+    {
+        const int i = min(i0, m - 1);
+        int lo = 0, hi = P - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= (uint32_t)i)
+                lo = mid;
+            else
+                hi = mid - 1;
         }
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int i = i0 + j * kFinThreads + tid;
-            if (i < (int)m)
-                cl[i] = e[j];
-        }
+        sl = lo;
     }
-    __syncthreads();
+    int src_off[kFinRun];
+#pragma unroll
+    for (int j = 0; j < kFinRun; j++) {
+        const int i = min(i0 + min(j, max(n_own - 1, 0)), m - 1);
+        while (sl + 1 < P && pre[sl + 1] <= (uint32_t)i)
+            sl++;
+        src_off[j] = sl * kSelSlice + (i - (int)pre[sl]);
+    }
+    const u32x2 *src = cand + (int64_t)r * stride;
+    uint32_t kk[kFinRun], id[kFinRun];
+#pragma unroll
+    for (int j = 0; j < kFinRun; j++) {
+        const u32x2 e = src[src_off[j]];
+        kk[j] = e.x;
+        id[j] = e.y;
+    }
 
     uint32_t above;
+    bool exact;
     const uint32_t T = block_kth_largest<kFinThreads>(
         [&](auto &&f) {
-            for (int i = tid; i < (int)m; i += kFinThreads)
-                f(cl[i].x);
+#pragma unroll
+            for (int j = 0; j < kFinRun; j++)
+                if (j < n_own)
+                    f(kk[j]);
         },
-        (uint32_t)top_k, hist, &bs, &above);
+        (uint32_t)top_k, hist, &bs, 3, &above, &exact);
     const uint32_t need_eq = (uint32_t)top_k - above; // keys == T to take, lowest index first
 
-    // each thread a contiguous run of candidates; one scan of the packed
-    // (equal, greater) counts places every selected id
-    const int run = ((int)m + kFinThreads - 1) / kFinThreads;
-    const int i0 = min(tid * run, (int)m);
-    const int i1 = min(i0 + run, (int)m);
+    // one scan of the packed (equal, greater) counts places every selected id
     uint32_t ngt = 0, neq = 0;
-    for (int i = i0; i < i1; i++) {
-        const uint32_t k = cl[i].x;
-        ngt += k > T ? 1u : 0u;
-        neq += k == T ? 1u : 0u;
+#pragma unroll
+    for (int j = 0; j < kFinRun; j++) {
+        if (j < n_own) {
+            ngt += kk[j] > T ? 1u : 0u;
+            neq += kk[j] == T ? 1u : 0u;
+        }
     }
     uint32_t tot;
     const uint32_t pk = block_exclusive_scan<kFinThreads>((neq << 16) | ngt, bs.scan, &tot);
     uint32_t eqi = pk >> 16;
     uint32_t pos = (pk & 0xFFFFu) + min(eqi, need_eq);
-    for (int i = i0; i < i1; i++) {
-        const u32x2 e = cl[i];
-        const bool take = e.x > T || (e.x == T && eqi < need_eq);
-        eqi += e.x == T ? 1u : 0u;
-        if (take && pos < (uint32_t)top_k)
-            out[pos++] = (int32_t)e.y;
+#pragma unroll
+    for (int j = 0; j < kFinRun; j++) {
+        if (j < n_own) {
+            const bool take = kk[j] > T || (kk[j] == T && eqi < need_eq);
+            eqi += kk[j] == T ? 1u : 0u;
+            if (take && pos < (uint32_t)top_k)
+                out[pos++] = (int32_t)id[j];
+        }
     }
 }
 
