@@ -99,6 +99,9 @@ def main() -> int:
                     help="input copies the steps rotate through (1 = warm caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--index-launches", type=int, default=50)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the index kernel and a plain 256 MiB device copy a few "
+                         "times each (for rocprofv3 counter passes), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -128,6 +131,25 @@ def main() -> int:
                      step.block_tables, step.seq_lens, step.kv_scale, step.sm_scale,
                      step.scores, step.sel, step.out, step.ws, stream=stream)
 
+    if args.traffic_probe:
+        # HBM counters read per dispatch: the index kernel, and a plain copy of
+        # known size that calibrates the counter's scale
+        copy_bytes = 256 << 20
+        src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(4):
+                dst.copy_(src)
+            for i in range(4):
+                dsa.index_scores(sh, step.q_idx, step.w, keys[i % nrep], step.seq_lens,
+                                 step.scores, stream=stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": copy_bytes,
+                          "index_algorithmic_bytes": algorithmic_bytes(inputs)["index"],
+                          "index_kernel_sha": kernel_sha()}), flush=True)
+        return 0
+
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             run(i)
@@ -147,23 +169,21 @@ def main() -> int:
         torch.cuda.synchronize()
         warm = time.perf_counter() - wt0
 
-        # dominant kernel: the index-score pass, timed per launch with HIP
-        # events recorded on the stream it runs on, inside step-shaped
-        # iterations (index, select, attend through the stage entry points,
-        # rotating replicas as the timed steps do)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.index_launches)]
-        for i, (a, b) in enumerate(evs):
-            a.record(stream)
+        # dominant kernel: the index-score pass, launched back to back on
+        # rotating replicas (cold keys, as in the timed steps) between one
+        # pair of HIP events on the stream it runs on; the mean per launch
+        # is the span over the launch count (no per-launch event gaps)
+        ev_a = torch.cuda.Event(enable_timing=True)
+        ev_b = torch.cuda.Event(enable_timing=True)
+        dsa.index_scores(sh, step.q_idx, step.w, keys[1 % nrep], step.seq_lens, step.scores,
+                         stream=stream)
+        ev_a.record(stream)
+        for i in range(args.index_launches):
             dsa.index_scores(sh, step.q_idx, step.w, keys[i % nrep], step.seq_lens, step.scores,
                              stream=stream)
-            b.record(stream)
-            dsa.topk_select(sh, step.scores, step.seq_lens, step.sel, step.ws, stream=stream)
-            dsa.mla_decode(sh, step.q, pools[i % nrep], step.block_tables, step.seq_lens,
-                           step.sel, step.kv_scale, step.sm_scale, step.out, step.ws,
-                           stream=stream)
+        ev_b.record(stream)
         torch.cuda.synchronize()
-        idx_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        idx_ms = ev_a.elapsed_time(ev_b) / args.index_launches
 
     ab = algorithmic_bytes(inputs)
     ms = elapsed / args.steps * 1e3
