@@ -97,6 +97,49 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
+// Wave-wide reductions and scan through DPP row moves plus three readlanes
+// (no LDS round trip): the sum / max / min of all 64 lanes in every lane, and
+// the inclusive prefix sum of lanes 0..lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_shift_in_zero(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_add(uint32_t x)
+{
+    x += dpp_shift_in_zero<0x111>(x); // row_shr:1
+    x += dpp_shift_in_zero<0x112>(x); // row_shr:2
+    x += dpp_shift_in_zero<0x114>(x); // row_shr:4
+    x += dpp_shift_in_zero<0x118>(x); // row_shr:8 -> prefix within each row of 16
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<kDppQuadXor1>(v));
+    v = max(v, dpp_u32<kDppQuadXor2>(v));
+    v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+    v = max(v, dpp_u32<kDppRowMirror>(v));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                   (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                   (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = min(v, dpp_u32<kDppQuadXor1>(v));
+    v = min(v, dpp_u32<kDppQuadXor2>(v));
+    v = min(v, dpp_u32<kDppRowHalfMirror>(v));
+    v = min(v, dpp_u32<kDppRowMirror>(v));
+    return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                   (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+               min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                   (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 // Block-wide exclusive prefix sum of one value per thread (blockDim.x == NT).
 // `scratch` holds NT/64 + 1 words of LDS. Returns the exclusive prefix; the
 // block total lands in *total.
@@ -107,13 +150,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     constexpr int NW = NT / kWave;
     const int lane = threadIdx.x % kWave;
     const int wid = threadIdx.x / kWave;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o)
-            x += y;
-    }
+    const uint32_t x = wave_incl_scan_add(v);
     if (lane == kWave - 1)
         scratch[wid] = x;
     __syncthreads();
@@ -121,7 +158,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     uint32_t tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; w++) {
-        uint32_t s = scratch[w];
+        const uint32_t s = scratch[w];
         base += (w < wid) ? s : 0u;
         tot += s;
     }

@@ -24,7 +24,7 @@ inline int sel_slices(const LaunchShape &ls) { return (ls.max_len + kSelSlice - 
 
 // Attention geometry: a row's selection is cut into chunks of kAttChunk
 // slots; a workgroup covers kAttHeads heads of one chunk.
-constexpr int kAttChunk = 256;
+constexpr int kAttChunk = 128;
 constexpr int kAttHeads = 64;
 
 // Row stride of the scores buffer: max_len rounded up to 64 floats, so every

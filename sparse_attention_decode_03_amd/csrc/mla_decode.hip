@@ -8,20 +8,24 @@
 //
 // Decomposition (a function of the row alone, never of R, so every row is
 // bit-reproducible whichever rows share a launch):
-//  - A row's selection is cut into chunks of 256 slots. One workgroup
-//    (4 waves x 16 heads = 64 heads) handles one chunk: it walks the chunk in
-//    steps of 32 tokens, gathering each token's 512-byte FP8 row through the
-//    block table with coalesced 16-byte loads, dequantising it exactly to
-//    bf16 (E4M3 is a subset of bf16; kv_scale is folded into the logit scale
-//    and the output) and parking the 32 x 512 tile in LDS, token-major, in
-//    padded rows that keep both operand reads below free of bank conflicts.
-//  - QK: S^T[token, head] on 16x16x32 bf16 MFMA, the tile as A (k = latent
-//    dim), Q as B (staged in LDS once per workgroup). The MFMA output leaves
-//    each lane with eight tokens of one head, which are exactly the k-slots
-//    of that lane's PV operand, so the probabilities never leave registers.
-//  - Online softmax in fp32 (log2 domain, exp2), fixed-order reductions.
-//  - PV: O[head, d] on 16x16x32 bf16 MFMA, P (bf16) as A, the tile as B read
-//    through LDS transpose loads (ds_read_tr16_b64), fp32 accumulators.
+//  - A row's selection is cut into chunks of kAttChunk slots. One workgroup
+//    of 4 waves covers one chunk for 64 heads. It walks the chunk in steps of
+//    32 tokens: each token's 512-byte FP8 row is gathered through the block
+//    table with coalesced 16-byte loads (two steps ahead), dequantised
+//    exactly to bf16 (E4M3 is a subset of bf16; kv_scale is folded into the
+//    logit scale and the output) and parked in one of two LDS tiles,
+//    token-major, in padded rows that keep the operand reads below free of
+//    bank conflicts. Two barriers per step.
+//  - QK + softmax, split by heads: wave w computes S^T[token, head] for
+//    heads 16w..16w+15 on 16x16x32 bf16 MFMA, the tile as A and the query
+//    (staged in LDS once per workgroup) as B. Online
+//    softmax in fp32 (log2 domain, exp2, fixed-order reductions, lazy
+//    rescale). The bf16 probabilities go to a small LDS buffer laid out in
+//    the PV operand's k order (one 16-byte write, one 16-byte read).
+//  - PV, split by latent columns: wave w accumulates O[all 64 heads,
+//    columns 128w..128w+127] on 16x16x32 bf16 MFMA, P as A, the tile as B
+//    through LDS transpose loads (ds_read_tr16_b64). Each wave thus reads a
+//    quarter of the tile instead of all of it.
 //  - A row with one chunk writes its bf16 output directly. Otherwise every
 //    chunk writes (m, l, O) partials and k_mla_merge folds them in chunk
 //    order 0, 1, 2, ... with the same fp32 formula for every row.
@@ -31,20 +35,23 @@
 namespace dsa {
 
 constexpr int kAttThreads = 256;
-constexpr int kStep = 32;          // tokens per LDS tile
-constexpr int kLat = 512;          // latent width
+constexpr int kStep = 32;            // tokens per LDS tile
+constexpr int kLat = 512;            // latent width
 constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 latent row (64)
-// LDS rows (a token's bf16 latent, or a head's bf16 query) are padded from
-// 1024 to 1072 bytes (67 chunks). With a 48-byte pad, 16 consecutive rows read
-// at one chunk start 12 words apart modulo the 64 banks (all distinct 4-word
-// groups), and the 4 consecutive rows x 4 eight-byte segments of one
-// transpose read land on 32 distinct banks. Addresses stay a lane base plus
-// compile-time offsets.
+// LDS tile rows (a token's bf16 latent) are padded from 1024 to 1072 bytes
+// (67 chunks). With a 48-byte pad, 16 consecutive rows read at one chunk
+// start 12 words apart modulo the 64 banks (all distinct 4-word groups), and
+// the 4 consecutive rows x 4 eight-byte segments of one transpose read land
+// on 32 distinct banks. Addresses stay a lane base plus compile-time offsets.
 constexpr int kRowStride = kRowChunks + 3; // in 16-byte chunks
+// Probability rows (one head, 32 bf16) are padded from 64 to 80 bytes: 16
+// consecutive heads read at one 16-byte column hit 16 distinct 4-bank groups.
+constexpr int kPRowBytes = 80;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
@@ -54,9 +61,13 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
-    __shared__ u32x4 tile[kStep * kRowStride];      // bf16 tokens x latent, padded rows
-    __shared__ u32x4 qlds[kAttHeads * kRowStride];  // bf16 Q of the 64 heads, padded rows
-    __shared__ int rowidx[kAttChunk];               // latent row of each slot, -1 = skip
+    __shared__ u32x4 tile[2][kStep * kRowStride];        // bf16 tokens x latent, padded rows
+    __shared__ u32x4 qlds[kAttHeads * kRowStride];       // bf16 query of the 64 heads, padded
+    __shared__ __align__(16) uint8_t pbuf[kAttHeads * kPRowBytes]; // bf16 P, PV k order
+    __shared__ float alds[kAttHeads];                    // per-head rescale factors
+    __shared__ float2 mlds[kAttHeads];                   // per-head (m, l) at the end
+    __shared__ int rowidx[kAttChunk];                    // latent row of each slot, -1 = skip
+    __shared__ int resc_step;                            // last step whose O needs a rescale
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -70,12 +81,15 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int L = min(max(seq_lens[r], 0), max_len);
     const int n = min(top_k, L);
     const int nch = (n + kAttChunk - 1) / kAttChunk;
-    const int h_base = hg * kAttHeads + wave * 16;
+    const int h0 = hg * kAttHeads;              // first head of the group
+    const int nh = min(kAttHeads, H - h0);      // heads of the group that exist
+    const int hq = h0 + wave * 16 + n16;        // this lane's head in QK
+    const bool qk_active = wave * 16 < nh;      // the wave's QK heads exist
 
     if (n == 0) {
         if (c == 0) {
             for (int i = tid; i < kAttHeads * kLat; i += kAttThreads) {
-                const int h = hg * kAttHeads + i / kLat;
+                const int h = h0 + i / kLat;
                 if (h < H)
                     out[((int64_t)r * H + h) * kLat + (i % kLat)] = 0;
             }
@@ -84,55 +98,58 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     }
     if (c >= nch)
         return;
-    const bool wave_active = h_base < H;
     const int slot0 = c * kAttChunk;
-    const int slot_end = min(n, slot0 + kAttChunk);
+    const int nslots = min(n - slot0, kAttChunk);
+    const int nsteps = (nslots + kStep - 1) / kStep;
 
     // ---- resolve the chunk's selected tokens to latent rows once ----
-    {
-        const int slot = slot0 + tid;
+    for (int k = tid; k < kAttChunk; k += kAttThreads) {
         int row = -1;
-        if (slot < slot_end) {
-            const int t = sel[(int64_t)r * top_k + slot];
+        if (k < nslots) {
+            const int t = sel[(int64_t)r * top_k + slot0 + k];
             if (t >= 0 && t < L) {
                 const int page = bt[(int64_t)s * max_blocks + t / ps];
                 if (page >= 0 && page < num_pages)
                     row = page * ps + t % ps;
             }
         }
-        rowidx[tid] = row;
+        rowidx[k] = row;
     }
+    if (tid == 0)
+        resc_step = -1;
 
-    // Q of the workgroup's 64 heads into LDS (padded head rows).
+    // ---- query of the group's 64 heads into LDS (padded head rows);
+    // branch-free, a missing head loads head H-1 and is zeroed ----
 #pragma unroll
     for (int i = 0; i < kAttHeads * kRowChunks / kAttThreads; i++) {
         const int id = i * kAttThreads + tid;
         const int hh = id / kRowChunks;
         const int ch = id % kRowChunks;
-        const int h = hg * kAttHeads + hh;
-        // branch-free: load a valid row, zero it if the head is padding
+        const int h = h0 + hh;
         u32x4 v = *(const u32x4 *)(q + ((int64_t)r * H + min(h, H - 1)) * kLat + ch * 8);
         if (h >= H)
             v = u32x4{0u, 0u, 0u, 0u};
         qlds[hh * kRowStride + ch] = v;
     }
-    __syncthreads();
 
-    float m_run = kNegInf; // running max of the log2-domain logits (head n16)
-    float l_run = 0.0f;    // running sum of exp2(z - m_run)
-    floatx4 o[32];
+    float m_run = kNegInf; // reference max of the log2-domain logits (head hq)
+    float l_run = 0.0f;    // this lane's share of sum exp2(z - m_run)
+    floatx4 o[4][8];       // O[head 16*mt + 4g + v][column 128*wave + 16*nt + n16]
 #pragma unroll
-    for (int nt = 0; nt < 32; nt++)
-        o[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int nt = 0; nt < 8; nt++)
+            o[mt][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    int mt_count = (nh + 15) / 16; // head tiles that exist
 
     const int tq = tid >> 5; // staging: tokens 4*tq .. 4*tq+3
     const int dc = tid & 31; //          latent bytes 16*dc .. 16*dc+15
 
     // One step's 32 FP8 rows into registers; two steps stay in flight.
-    auto gather = [&](u32x4 (&raw)[4], int base) {
+    auto gather = [&](u32x4 (&raw)[4], int step) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int k = base - slot0 + 4 * tq + i;
+            const int k = step * kStep + 4 * tq + i;
             const int row = (k < kAttChunk) ? rowidx[k] : -1;
             // branch-free so the four loads issue back to back: a skipped
             // slot reads latent row 0 and is zeroed
@@ -141,8 +158,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 raw[i] = u32x4{0u, 0u, 0u, 0u};
         }
     };
-    // Dequantise (exact) into the bf16 LDS tile.
-    auto stage = [&](const u32x4 (&raw)[4]) {
+    // Dequantise (exact) into LDS tile b.
+    auto stage = [&](const u32x4 (&raw)[4], int b) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * tq + i;
@@ -155,35 +172,43 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
             hi.y = e4m3x2_to_bf16x2_exact<true>(raw[i].z);
             hi.z = e4m3x2_to_bf16x2_exact<false>(raw[i].w);
             hi.w = e4m3x2_to_bf16x2_exact<true>(raw[i].w);
-            tile[t * kRowStride + 2 * dc] = lo;
-            tile[t * kRowStride + 2 * dc + 1] = hi;
+            tile[b][t * kRowStride + 2 * dc] = lo;
+            tile[b][t * kRowStride + 2 * dc + 1] = hi;
         }
     };
-    // QK, online softmax and PV over the staged tile of step `base`.
-    auto compute = [&](int base) {
-        // ---- QK: lane ends with head n16, tokens 8g + 4a + v ----
-        // ---- QK: S^T[token][head], tile rows as A (token 16a + n16, k =
-        // latent dims 32*ks + 8*g .. +7), Q as B (head wave*16 + n16); the
-        // lane ends with head n16 and tokens 16a + 4g + v (v = 0..3) ----
+
+    // QK and online softmax of step `step` (tile b) for this wave's heads;
+    // leaves P in pbuf and, on a step where a reference moved, the alphas.
+    auto qk_softmax = [&](int step, int b) {
         floatx4 sacc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
-        {
-            const u32x4 *qrow = qlds + (wave * 16 + n16) * kRowStride + g;
-            const u32x4 *t0row = tile + n16 * kRowStride + g;
-            const u32x4 *t1row = tile + (16 + n16) * kRowStride + g;
+        // A: tile rows n16 and 16 + n16, k = latent dims 32*ks + 8*g .. +7;
+        // B: query of head wave*16 + n16 with the same k order. Operands of
+        // four k-steps are read ahead of their products.
+        const u32x4 *t0row = tile[b] + n16 * kRowStride + g;
+        const u32x4 *t1row = tile[b] + (16 + n16) * kRowStride + g;
+        const u32x4 *qrow = qlds + (wave * 16 + n16) * kRowStride + g;
 #pragma unroll
-            for (int ks = 0; ks < 16; ks++) {
-                const bf16x8 qv = as_bf16x8(qrow[4 * ks]);
-                sacc[0] = mfma16x16x32(as_bf16x8(t0row[4 * ks]), qv, sacc[0]);
-                sacc[1] = mfma16x16x32(as_bf16x8(t1row[4 * ks]), qv, sacc[1]);
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+            u32x4 a0[4], a1[4], qb[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                a0[j] = t0row[4 * (k0 + j)];
+                a1[j] = t1row[4 * (k0 + j)];
+                qb[j] = qrow[4 * (k0 + j)];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                sacc[0] = mfma16x16x32(as_bf16x8(a0[j]), as_bf16x8(qb[j]), sacc[0]);
+                sacc[1] = mfma16x16x32(as_bf16x8(a1[j]), as_bf16x8(qb[j]), sacc[1]);
             }
         }
-        // ---- online softmax (log2 domain) ----
+        // lane: head hq, tokens 16*(j>>2) + 4g + (j&3) for j = 0..7
         float z[8];
         float mx = kNegInf;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const float v = sacc[j >> 2][j & 3] * qk_log2;
-            z[j] = rowidx[base - slot0 + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
+            z[j] = rowidx[step * kStep + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
             mx = __builtin_fmaxf(mx, z[j]);
         }
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -205,102 +230,135 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
             p[j] = exp2f(z[j] - m_use);
             rs += p[j];
         }
-        rs += __shfl_xor(rs, 16, kWave);
-        rs += __shfl_xor(rs, 32, kWave);
         l_run = __builtin_fmaf(l_run, alpha, rs);
-        // O rows are heads 4g + v: rescale them by their own alpha, only on a
-        // step where some head's reference moved (otherwise every alpha is
-        // exactly 1, or O is still zero, and the multiply changes nothing)
-        const bool grew = __ballot(move && m_run != kNegInf) != 0;
+        // every step leaves its alphas (1 where nothing moved); the PV waves
+        // apply them only on a step marked here
+        if (g == 0)
+            alds[wave * 16 + n16] = alpha;
+        if (__ballot(move && m_run != kNegInf) != 0 && lane == 0)
+            resc_step = step;
         m_run = m_new;
-        if (grew) {
-            float av[4];
-#pragma unroll
-            for (int v = 0; v < 4; v++)
-                av[v] = __shfl(alpha, 4 * g + v, kWave);
-#pragma unroll
-            for (int nt = 0; nt < 32; nt++) {
-                o[nt][0] *= av[0];
-                o[nt][1] *= av[1];
-                o[nt][2] *= av[2];
-                o[nt][3] *= av[3];
-            }
-        }
         u32x4 pw;
         pw.x = pack_bf16x2(p[0], p[1]);
         pw.y = pack_bf16x2(p[2], p[3]);
         pw.z = pack_bf16x2(p[4], p[5]);
         pw.w = pack_bf16x2(p[6], p[7]);
-        const bf16x8 pa = as_bf16x8(pw);
-        // ---- PV: O[head][d] += P[head][token] C[token][d]; P as A (k-slot
-        // j <-> token 16(j>>2) + 4g + (j&3), exactly the tokens this lane's
-        // softmax holds), the tile as B through two transpose loads of 4
-        // consecutive rows each: lane n16 receives latent column 16*nt + n16 ----
-        const char *tb = (const char *)tile;
-        const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3);
+        *(u32x4 *)(pbuf + (wave * 16 + n16) * kPRowBytes + 16 * g) = pw;
+    };
+
+    // PV of step `step` (tile b): O[heads, this wave's 128 columns]. P as A
+    // (k-slot j <-> token 16(j>>2) + 4g + (j&3)), the tile as B through two
+    // transpose loads of 4 consecutive rows each: lane n16 receives column
+    // 128*wave + 16*nt + n16, rows 4g..4g+3 and 16+4g..16+4g+3.
+    auto pv = [&](int step, int b) {
+        const bool resc = resc_step == step;
+        const char *tb = (const char *)tile[b];
+        const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3) + 256 * wave;
         const char *p1 = p0 + 16 * (kRowStride * 16);
+        shortx8 vb[8];
 #pragma unroll
-        for (int nt = 0; nt < 32; nt++) {
+        for (int nt = 0; nt < 8; nt++) {
             const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p0 + 32 * nt));
             const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p1 + 32 * nt));
-            typedef short shortx8 __attribute__((ext_vector_type(8)));
-            const shortx8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-            o[nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, bb), o[nt]);
+            vb[nt] = shortx8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+            if (mt < mt_count) {
+                const bf16x8 pa = as_bf16x8(*(const u32x4 *)(pbuf + (16 * mt + n16) * kPRowBytes + 16 * g));
+                if (resc) {
+                    const floatx4 av = *(const floatx4 *)(alds + 16 * mt + 4 * g);
+#pragma unroll
+                    for (int nt = 0; nt < 8; nt++) {
+                        o[mt][nt][0] *= av[0];
+                        o[mt][nt][1] *= av[1];
+                        o[mt][nt][2] *= av[2];
+                        o[mt][nt][3] *= av[3];
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < 8; nt++)
+                    o[mt][nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, vb[nt]), o[mt][nt]);
+            }
         }
     };
 
+    __syncthreads(); // rowidx and resc_step visible
     u32x4 ra[4], rb[4];
-    gather(ra, slot0);
-    if (slot0 + kStep < slot_end)
-        gather(rb, slot0 + kStep);
-    for (int base = slot0; base < slot_end; base += 2 * kStep) {
-        stage(ra);
-        __syncthreads();
-        if (base + 2 * kStep < slot_end)
-            gather(ra, base + 2 * kStep);
-        if (wave_active)
-            compute(base);
-        __syncthreads();
-        if (base + kStep >= slot_end)
+    gather(ra, 0);
+    if (nsteps > 1)
+        gather(rb, 1);
+    stage(ra, 0);
+    if (nsteps > 2)
+        gather(ra, 2);
+    // step i computes from tile i & 1; during step i the next step's rows
+    // are staged into the other tile and the rows of step i + 3 are gathered
+    for (int i = 0; i < nsteps; i += 2) {
+        __syncthreads(); // tile 0 holds step i; PV of step i - 1 is done
+        if (qk_active)
+            qk_softmax(i, 0);
+        if (i + 1 < nsteps) {
+            stage(rb, 1);
+            if (i + 3 < nsteps)
+                gather(rb, i + 3);
+        }
+        __syncthreads(); // P of step i visible
+        pv(i, 0);
+        if (i + 1 >= nsteps)
             break;
-        stage(rb);
+        __syncthreads(); // tile 1 holds step i + 1; PV of step i is done
+        if (qk_active)
+            qk_softmax(i + 1, 1);
+        if (i + 2 < nsteps) {
+            stage(ra, 0);
+            if (i + 4 < nsteps)
+                gather(ra, i + 4);
+        }
         __syncthreads();
-        if (base + 3 * kStep < slot_end)
-            gather(rb, base + 3 * kStep);
-        if (wave_active)
-            compute(base + kStep);
-        __syncthreads();
+        pv(i + 1, 1);
     }
 
-    if (!wave_active)
-        return;
+    // ---- per-head (m, l): the four lanes of a head hold shares of l ----
+    const float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+    const float l_all = l_tot + __shfl_xor(l_tot, 32, kWave);
+    if (qk_active && g == 0)
+        mlds[wave * 16 + n16] = float2{m_run, l_all};
+    __syncthreads();
+
     if (nch == 1) {
-        float inv[4];
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const float lh = __shfl(l_run, 4 * g + v, kWave);
-            inv[v] = lh > 0.0f ? kv_scale / lh : 0.0f;
-        }
+        for (int mt = 0; mt < 4; mt++) {
+            if (mt >= mt_count)
+                break;
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const int h = h_base + 4 * g + v;
-            if (h < H) {
-                uint16_t *orow = out + ((int64_t)r * H + h) * kLat;
+            for (int v = 0; v < 4; v++) {
+                const int hl = 16 * mt + 4 * g + v;
+                const int h = h0 + hl;
+                if (h < H) {
+                    const float lh = mlds[hl].y;
+                    const float inv = lh > 0.0f ? kv_scale / lh : 0.0f;
+                    uint16_t *orow = out + ((int64_t)r * H + h) * kLat + 128 * wave + n16;
 #pragma unroll
-                for (int nt = 0; nt < 32; nt++)
-                    orow[16 * nt + n16] = f32_to_bf16_rne(o[nt][v] * inv[v]);
+                    for (int nt = 0; nt < 8; nt++)
+                        orow[16 * nt] = f32_to_bf16_rne(o[mt][nt][v] * inv);
+                }
             }
         }
     } else {
         const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
-        if (g == 0)
-            part_ml[pbase + wave * 16 + n16] = float2{m_run, l_run};
+        if (qk_active && g == 0)
+            part_ml[pbase + wave * 16 + n16] = float2{m_run, l_all};
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            float *prow = part_o + (pbase + wave * 16 + 4 * g + v) * kLat;
+        for (int mt = 0; mt < 4; mt++) {
+            if (mt >= mt_count)
+                break;
 #pragma unroll
-            for (int nt = 0; nt < 32; nt++)
-                prow[16 * nt + n16] = o[nt][v];
+            for (int v = 0; v < 4; v++) {
+                float *prow = part_o + (pbase + 16 * mt + 4 * g + v) * kLat + 128 * wave + n16;
+#pragma unroll
+                for (int nt = 0; nt < 8; nt++)
+                    prow[16 * nt] = o[mt][nt][v];
+            }
         }
     }
 }

@@ -43,12 +43,15 @@ constexpr int kSliceThreads = 256;          // filter workgroup
 constexpr int kSliceTokPerThread = kSelSlice / kSliceThreads; // 16
 constexpr int kGmRegs = 32;                 // group keys a filter thread keeps in registers
 constexpr int kFinThreads = 1024;           // finishing workgroup
-constexpr int kFinCap = 16384;              // candidates the finishing workgroup holds
+constexpr int kFinCap = 8192;               // candidates the finishing workgroup holds
 constexpr int kRowThreads = kFinThreads;    // full-row fallback runs in the same workgroup
 constexpr int kRowWaves = kRowThreads / kWave;
 constexpr int kVecBatch = 8;                // float4 loads per thread per batch (full row)
 constexpr int kCandCap = 6144;              // full-row candidates kept in LDS (48 KiB)
 constexpr int kBitmapLdsWords = 12288;      // full-row bitmap in LDS up to 393216 tokens
+constexpr int kSelDigit = 12;               // bits of a threshold / cut digit
+constexpr int kSelBins = 1 << kSelDigit;    // its histogram bins
+constexpr int kRankList = 256;              // boundary-bin members ranked directly
 
 // Shared state of block-wide searches and reductions.
 struct BinSearch {
@@ -99,16 +102,14 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
     return b;
 }
 
-// Block-wide minimum and maximum of one pair per thread.
+// Block-wide minimum and maximum of one pair per thread (one barrier; call
+// at most once per kernel, as the exchange words are not guarded for reuse).
 template <int NT>
 __device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
 {
     constexpr int NW = NT / kWave;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, kWave));
-    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
     const int wid = threadIdx.x / kWave;
     if (threadIdx.x % kWave == 0) {
         bs->red[0][wid] = lo;
@@ -120,121 +121,60 @@ __device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
         lo = min(lo, bs->red[0][w]);
         hi = max(hi, bs->red[1][w]);
     }
-    __syncthreads();
 }
 
-// Descending walk over the kHistBins-bin LDS histogram h (16-byte aligned):
+// Descending walk over the kSelBins-bin LDS histogram h (16-byte aligned):
 // the bin where the running count first reaches `need`, and the count of
-// everything above it, into bs. Run by wave 0 alone (32 bins per lane, one
-// lane scan); a barrier of the caller publishes the result. An inconsistent
-// histogram (total < need) yields bin 0.
+// everything above it, into bs. Run by wave 0 alone (64 bins per lane, one
+// DPP lane scan); a barrier of the caller publishes the result. An
+// inconsistent histogram (total < need) yields bin 0.
 __device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t need,
                                                     BinSearch *bs)
 {
-    constexpr int BPL = kHistBins / kWave; // 32
+    constexpr int BPL = kSelBins / kWave; // 64
     const int lane = threadIdx.x;
-    const int lo_b = kHistBins - BPL * (lane + 1); // lane 0 holds the top bins
-    uint32_t c[BPL];
-#pragma unroll
-    for (int q = 0; q < BPL / 4; q++) {
-        const u32x4 v = *(const u32x4 *)(h + lo_b + 4 * q);
-        c[4 * q] = v.x;
-        c[4 * q + 1] = v.y;
-        c[4 * q + 2] = v.z;
-        c[4 * q + 3] = v.w;
-    }
+    const int lo_b = kSelBins - BPL * (lane + 1); // lane 0 holds the top bins
+    const u32x4 *h4 = (const u32x4 *)(h + lo_b);
     uint32_t local = 0;
 #pragma unroll
-    for (int i = 0; i < BPL; i++)
-        local += c[i];
-    uint32_t x = local;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, o, kWave);
-        if (lane >= o)
-            x += y;
+    for (int q = 0; q < BPL / 4; q++) {
+        const u32x4 v = h4[q];
+        local += (v.x + v.y) + (v.z + v.w);
     }
+    const uint32_t x = wave_incl_scan_add(local);
     const uint32_t run = x - local; // count in the bins of lower lanes (higher bins)
     if (lane == 0) {
         bs->bin = 0u;
         bs->before = 0u;
     }
-    if (run < need && x >= need) { // exactly one lane
+    if (run < need && x >= need) { // exactly one lane: walk its bins downwards
         uint32_t bef = run;
         uint32_t bin = (uint32_t)lo_b;
-        bool found = false;
+        for (int q = BPL / 4 - 1; q >= 0; q--) {
+            const u32x4 v = h4[q];
+            const uint32_t cq[4] = {v.x, v.y, v.z, v.w};
+            bool found = false;
 #pragma unroll
-        for (int i = BPL - 1; i >= 0; i--) {
-            if (!found) {
-                if (bef + c[i] >= need) {
-                    bin = (uint32_t)(lo_b + i);
-                    found = true;
-                } else {
-                    bef += c[i];
+            for (int i = 3; i >= 0; i--) {
+                if (!found) {
+                    if (bef + cq[i] >= need) {
+                        bin = (uint32_t)(lo_b + 4 * q + i);
+                        found = true;
+                    } else {
+                        bef += cq[i];
+                    }
                 }
             }
+            if (found)
+                break;
         }
         bs->bin = bin;
         bs->before = bef;
     }
 }
 
-// Radix selection of the rank-th largest key (1 <= rank <= number of keys)
-// among the keys the block's threads visit through for_keys(f) (f(key) once
-// per key; each thread visits its own share). Digits of up to 11 bits are
-// taken relative to the block's minimum key, from the top of the key range
-// down; `hist` is two LDS histograms (one counts while the other is cleared),
-// so a pass costs two barriers. After at most max_passes passes, returns the
-// lower end of the remaining key window: every key >= it is counted, at
-// least `rank` keys are >= it, and no key >= it is below the rank-th largest
-// key's window. *exact tells whether the window shrank to the single key T =
-// the rank-th largest (always so for max_passes >= 3); then *above counts
-// the keys greater than T. All NT threads must call.
-template <int NT, class ForKeys>
-__device__ uint32_t block_kth_largest(ForKeys for_keys, uint32_t rank,
-                                      uint32_t (*hist)[kHistBins], BinSearch *bs, int max_passes,
-                                      uint32_t *above_out, bool *exact)
-{
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for_keys([&](uint32_t k) {
-        lo = min(lo, k);
-        hi = max(hi, k);
-    });
-    for (int i = threadIdx.x; i < kHistBins; i += NT)
-        hist[0][i] = 0u;
-    block_minmax<NT>(lo, hi, bs); // its barriers also publish the cleared hist[0]
-    uint32_t base = lo;
-    int bits = hi > lo ? 32 - __clz(hi - lo) : 0; // hi - lo < 2^bits
-    uint32_t need = rank;
-    uint32_t above = 0;
-    for (int pass = 0; bits > 0 && pass < max_passes; pass++) {
-        uint32_t *h = hist[pass & 1];
-        const int shift = bits > 11 ? bits - 11 : 0;
-        const uint32_t nb = 1u << (bits - shift);
-        // window [base, base + 2^bits): keys above it were counted before
-        for_keys([&](uint32_t k) {
-            const uint32_t d = (k - base) >> shift;
-            if (k >= base && d < nb)
-                atomicAdd(&h[d], 1u);
-        });
-        __syncthreads();
-        uint32_t *other = hist[(pass + 1) & 1];
-        for (int i = threadIdx.x; i < kHistBins; i += NT)
-            other[i] = 0u;
-        if (threadIdx.x < kWave)
-            find_bin_desc_wave0(h, need, bs);
-        __syncthreads();
-        const uint32_t b = bs->bin;
-        const uint32_t bef = bs->before;
-        need -= bef;
-        above += bef;
-        base += b << shift;
-        bits = shift;
-    }
-    *above_out = above;
-    *exact = bits == 0;
-    return base;
-}
+// Bit length of x (0 for 0).
+__device__ __forceinline__ int bit_len(uint32_t x) { return x ? 32 - __clz(x) : 0; }
 
 __device__ __forceinline__ int row_len(const int32_t *seq_lens, int r, int max_len)
 {
@@ -288,7 +228,7 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
     u32x2 *__restrict__ cand, uint32_t *__restrict__ cnt, int max_len, int stride, int top_k,
     int pmax)
 {
-    __shared__ __align__(16) uint32_t hist[2][kHistBins];
+    __shared__ __align__(16) uint32_t hist[kSelBins];
     __shared__ BinSearch bs;
     const int r = blockIdx.y;
     const int p = blockIdx.x;
@@ -307,8 +247,8 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
     for (int j = 0; j < 4; j++)
         v[j] = row4[min(t0 / 4 + j, nvec - 1)];
 
-    // tau from the finest group level that still has at least top_k groups
-    // and whose keys fit the registers; failing both, every token is a
+    // group keys: the finest level that still has at least top_k groups and
+    // whose keys fit the registers; failing both, every token is a
     // candidate (then L < 4 top_k)
     const int ng32 = (L + 31) / 32;
     const int ng4 = (L + 3) / 4;
@@ -324,34 +264,45 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
         gm = gm4 + (int64_t)r * (stride / 4);
         ng = ng4;
     }
-    // two digit passes leave a window of at most 2^10 keys; its lower end
-    // is a valid threshold (at least top_k group keys are >= it)
+    // tau: the lower edge of the 12-bit digit bin (relative to the group
+    // keys' range) that holds the top_k-th largest group key. Every group
+    // key of that bin and above is >= tau, so at least top_k tokens are.
     uint32_t tau = 0u;
     if (gm != nullptr) {
-        uint32_t above;
-        bool exact;
-        if (ng <= kGmRegs * kSliceThreads) {
-            const int nj = (ng + kSliceThreads - 1) / kSliceThreads;
-            uint32_t kk[kGmRegs];
+        const bool in_regs = ng <= kGmRegs * kSliceThreads;
+        const int nj = (ng + kSliceThreads - 1) / kSliceThreads;
+        uint32_t kk[kGmRegs];
+        if (in_regs) {
 #pragma unroll
             for (int j = 0; j < kGmRegs; j++)
                 kk[j] = gm[min(tid + kSliceThreads * j, ng - 1)];
-            tau = block_kth_largest<kSliceThreads>(
-                [&](auto &&f) {
-#pragma unroll
-                    for (int j = 0; j < kGmRegs; j++)
-                        if (j < nj && tid + kSliceThreads * j < ng)
-                            f(kk[j]);
-                },
-                (uint32_t)top_k, hist, &bs, 2, &above, &exact);
-        } else {
-            tau = block_kth_largest<kSliceThreads>(
-                [&](auto &&f) {
-                    for (int i = tid; i < ng; i += kSliceThreads)
-                        f(gm[i]);
-                },
-                (uint32_t)top_k, hist, &bs, 2, &above, &exact);
         }
+        auto for_keys = [&](auto &&f) {
+            if (in_regs) {
+#pragma unroll
+                for (int j = 0; j < kGmRegs; j++)
+                    if (j < nj && tid + kSliceThreads * j < ng)
+                        f(kk[j]);
+            } else {
+                for (int i = tid; i < ng; i += kSliceThreads)
+                    f(gm[i]);
+            }
+        };
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        for_keys([&](uint32_t k) {
+            lo = min(lo, k);
+            hi = max(hi, k);
+        });
+        for (int i = tid; i < kSelBins; i += kSliceThreads)
+            hist[i] = 0u;
+        block_minmax<kSliceThreads>(lo, hi, &bs); // its barrier also publishes the cleared bins
+        const int shift = max(bit_len(hi - lo) - kSelDigit, 0);
+        for_keys([&](uint32_t k) { atomicAdd(&hist[(k - lo) >> shift], 1u); });
+        __syncthreads();
+        if (tid < kWave)
+            find_bin_desc_wave0(hist, (uint32_t)top_k, &bs);
+        __syncthreads();
+        tau = lo + (bs.bin << shift);
     }
 
     uint32_t key[kSliceTokPerThread];
@@ -595,17 +546,18 @@ __device__ void select_row_full(const float *__restrict__ scores, int r, int L, 
 // Finish: one workgroup per row. Thread t owns the contiguous run of
 // candidates [t * run, t * run + run) in registers (run <= 16), so the
 // selected ids leave in ascending order straight from registers.
-constexpr int kFinRun = kFinCap / kFinThreads; // 16
+constexpr int kFinRun = kFinCap / kFinThreads; // 8
 constexpr int kFullLdsBytes = 4 * kHistBins * 4 + kCandCap * 8 + kBitmapLdsWords * 4;
+static_assert(2 * kSelBins * 4 + kRankList * 8 <= kFullLdsBytes, "cut LDS must fit the area");
 
 __global__ __launch_bounds__(kFinThreads) void k_select_finish(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
     u32x2 *__restrict__ cand, const uint32_t *__restrict__ cnt, int32_t *__restrict__ sel,
     uint32_t *__restrict__ gbitmap, int max_len, int stride, int top_k, int pmax)
 {
-    __shared__ __align__(16) uint8_t area[kFullLdsBytes]; // full-row fallback only
+    __shared__ __align__(16) uint8_t area[kFullLdsBytes]; // full-row fallback, or the cut's
+                                                          // histograms and member list
     __shared__ uint32_t pre[kFinThreads];
-    __shared__ __align__(16) uint32_t hist[2][kHistBins];
     __shared__ BinSearch bs;
     __shared__ uint32_t ccount;
 
@@ -675,39 +627,121 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         id[j] = e.y;
     }
 
-    uint32_t above;
-    bool exact;
-    const uint32_t T = block_kth_largest<kFinThreads>(
-        [&](auto &&f) {
-#pragma unroll
-            for (int j = 0; j < kFinRun; j++)
-                if (j < n_own)
-                    f(kk[j]);
-        },
-        (uint32_t)top_k, hist, &bs, 3, &above, &exact);
-    const uint32_t need_eq = (uint32_t)top_k - above; // keys == T to take, lowest index first
-
-    // one scan of the packed (equal, greater) counts places every selected id
-    uint32_t ngt = 0, neq = 0;
+    // ---- exact cut: relative 12-bit digits narrow a key window to the
+    // bin holding the top_k-th candidate; the bin's members are then ranked
+    // directly under (key desc, index asc) ----
+    uint32_t *hist0 = (uint32_t *)area;                   // two histograms,
+    uint32_t *hist1 = (uint32_t *)(area + kSelBins * 4);  // then the member list
+    u32x2 *list = (u32x2 *)(area + 2 * kSelBins * 4);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int j = 0; j < kFinRun; j++) {
         if (j < n_own) {
-            ngt += kk[j] > T ? 1u : 0u;
-            neq += kk[j] == T ? 1u : 0u;
+            lo = min(lo, kk[j]);
+            hi = max(hi, kk[j]);
         }
     }
-    uint32_t tot;
-    const uint32_t pk = block_exclusive_scan<kFinThreads>((neq << 16) | ngt, bs.scan, &tot);
-    uint32_t eqi = pk >> 16;
-    uint32_t pos = (pk & 0xFFFFu) + min(eqi, need_eq);
+    for (int i = tid; i < kSelBins; i += kFinThreads)
+        hist0[i] = 0u;
+    if (tid == 0)
+        ccount = 0u;
+    block_minmax<kFinThreads>(lo, hi, &bs); // its barrier publishes the cleared bins
+    uint32_t base = lo;
+    int bits = bit_len(hi - lo); // window [base, base + 2^bits) holds every key
+    uint32_t need = (uint32_t)top_k;
+    uint32_t bin_lo = base;      // the boundary bin [bin_lo, bin_lo + 2^shift)
+    int shift = 0;
+    uint32_t count_b = (uint32_t)m;
+    uint32_t *h = hist0, *hn = hist1;
+    while (true) {
+        shift = max(bits - kSelDigit, 0);
+#pragma unroll
+        for (int j = 0; j < kFinRun; j++) {
+            if (j < n_own && kk[j] >= base) {
+                const uint32_t d = (kk[j] - base) >> shift;
+                if (d < (uint32_t)kSelBins)
+                    atomicAdd(&h[d], 1u);
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < kSelBins; i += kFinThreads)
+            hn[i] = 0u;
+        if (tid < kWave)
+            find_bin_desc_wave0(h, need, &bs);
+        __syncthreads();
+        const uint32_t b = bs.bin;
+        need -= bs.before;           // members of bin b to take
+        count_b = h[b];
+        bin_lo = base + (b << shift);
+        if (count_b <= (uint32_t)kRankList || shift == 0)
+            break;
+        base = bin_lo;
+        bits = shift;
+        uint32_t *t = h;
+        h = hn;
+        hn = t;
+        __syncthreads(); // everyone has read h[b] before it is cleared again
+    }
+    // keys >= bin_lo + 2^shift are taken, keys < bin_lo are not; the bin's
+    // members take `need` places
+    uint32_t take = 0; // bit j: owned candidate j is selected
+    uint32_t inbin = 0;
 #pragma unroll
     for (int j = 0; j < kFinRun; j++) {
-        if (j < n_own) {
-            const bool take = kk[j] > T || (kk[j] == T && eqi < need_eq);
-            eqi += kk[j] == T ? 1u : 0u;
-            if (take && pos < (uint32_t)top_k)
-                out[pos++] = (int32_t)id[j];
+        if (j < n_own && kk[j] >= bin_lo) {
+            if (((kk[j] - bin_lo) >> shift) >= 1u)
+                take |= 1u << j;
+            else
+                inbin |= 1u << j;
         }
+    }
+    if (count_b <= (uint32_t)kRankList) {
+        // few members: each ranks itself against the member list
+#pragma unroll
+        for (int j = 0; j < kFinRun; j++) {
+            if (inbin & (1u << j)) {
+                const uint32_t at = atomicAdd(&ccount, 1u);
+                if (at < (uint32_t)kRankList)
+                    list[at] = u32x2{kk[j], id[j]};
+            }
+        }
+        __syncthreads();
+        const uint32_t nl = min(ccount, (uint32_t)kRankList);
+#pragma unroll
+        for (int j = 0; j < kFinRun; j++) {
+            if (inbin & (1u << j)) {
+                uint32_t rank = 0;
+                for (uint32_t i = 0; i < nl; i++) {
+                    const u32x2 y = list[i];
+                    rank += (y.x > kk[j] || (y.x == kk[j] && y.y < id[j])) ? 1u : 0u;
+                }
+                if (rank < need)
+                    take |= 1u << j;
+            }
+        }
+    } else {
+        // one key shared by many members (shift == 0): lowest indices first;
+        // runs are in ascending index order, so a scan of member counts
+        // ranks them
+        uint32_t tot;
+        uint32_t rank = block_exclusive_scan<kFinThreads>((uint32_t)__popc(inbin), bs.scan, &tot);
+#pragma unroll
+        for (int j = 0; j < kFinRun; j++) {
+            if (inbin & (1u << j)) {
+                if (rank < need)
+                    take |= 1u << j;
+                rank++;
+            }
+        }
+    }
+
+    // ascending ids: one scan of the per-thread counts places every id
+    uint32_t tot;
+    uint32_t pos = block_exclusive_scan<kFinThreads>((uint32_t)__popc(take), bs.scan, &tot);
+#pragma unroll
+    for (int j = 0; j < kFinRun; j++) {
+        if ((take & (1u << j)) && pos < (uint32_t)top_k)
+            out[pos++] = (int32_t)id[j];
     }
 }
 
