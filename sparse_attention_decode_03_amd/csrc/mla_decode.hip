@@ -384,8 +384,9 @@ __global__ __launch_bounds__(128) void k_mla_merge(const float *__restrict__ par
     float m_acc = kNegInf, l_acc = 0.0f;
     floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     // partials are loaded in unrolled batches (independent loads in flight),
-    // then folded strictly in chunk order
-    constexpr int kB = 8;
+    // then folded strictly in chunk order; straight-line code with selects,
+    // so the batch stays in registers
+    constexpr int kB = 16;
     for (int c0 = 0; c0 < nch; c0 += kB) {
         float2 ml[kB];
         floatx4 ov[kB];
@@ -399,18 +400,17 @@ __global__ __launch_bounds__(128) void k_mla_merge(const float *__restrict__ par
         }
 #pragma unroll
         for (int k = 0; k < kB; k++) {
-            if (c0 + k >= nch)
-                break;
             const float m_new = __builtin_fmaxf(m_acc, ml[k].x);
-            if (m_new == kNegInf)
-                continue;
-            const float a = exp2f(m_acc - m_new);
-            const float b = exp2f(ml[k].x - m_new);
-            l_acc = __builtin_fmaf(ml[k].y, b, l_acc * a);
+            // a chunk past the last, or one with nothing selected so far,
+            // leaves the state untouched
+            const bool use = (c0 + k < nch) && (m_new != kNegInf);
+            const float a = use ? exp2f(m_acc - m_new) : 1.0f;
+            const float b = use ? exp2f(ml[k].x - m_new) : 0.0f;
+            l_acc = use ? __builtin_fmaf(ml[k].y, b, l_acc * a) : l_acc;
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                acc[i] = __builtin_fmaf(ov[k][i], b, acc[i] * a);
-            m_acc = m_new;
+                acc[i] = use ? __builtin_fmaf(ov[k][i], b, acc[i] * a) : acc[i];
+            m_acc = use ? m_new : m_acc;
         }
     }
     const float inv = l_acc > 0.0f ? kv_scale / l_acc : 0.0f;

@@ -135,11 +135,13 @@ __device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t 
     const int lane = threadIdx.x;
     const int lo_b = kSelBins - BPL * (lane + 1); // lane 0 holds the top bins
     const u32x4 *h4 = (const u32x4 *)(h + lo_b);
+    uint32_t qs[BPL / 4]; // per-quad sums of this lane's bins
     uint32_t local = 0;
 #pragma unroll
     for (int q = 0; q < BPL / 4; q++) {
         const u32x4 v = h4[q];
-        local += (v.x + v.y) + (v.z + v.w);
+        qs[q] = (v.x + v.y) + (v.z + v.w);
+        local += qs[q];
     }
     const uint32_t x = wave_incl_scan_add(local);
     const uint32_t run = x - local; // count in the bins of lower lanes (higher bins)
@@ -147,26 +149,35 @@ __device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t 
         bs->bin = 0u;
         bs->before = 0u;
     }
-    if (run < need && x >= need) { // exactly one lane: walk its bins downwards
-        uint32_t bef = run;
-        uint32_t bin = (uint32_t)lo_b;
-        for (int q = BPL / 4 - 1; q >= 0; q--) {
-            const u32x4 v = h4[q];
-            const uint32_t cq[4] = {v.x, v.y, v.z, v.w};
-            bool found = false;
+    if (run < need && x >= need) { // exactly one lane: its quads downwards in
+        uint32_t bef = run;        // registers, then the one quad from LDS
+        int qf = 0;
+        bool found = false;
 #pragma unroll
-            for (int i = 3; i >= 0; i--) {
-                if (!found) {
-                    if (bef + cq[i] >= need) {
-                        bin = (uint32_t)(lo_b + 4 * q + i);
-                        found = true;
-                    } else {
-                        bef += cq[i];
-                    }
+        for (int q = BPL / 4 - 1; q >= 0; q--) {
+            if (!found) {
+                if (bef + qs[q] >= need) {
+                    qf = q;
+                    found = true;
+                } else {
+                    bef += qs[q];
                 }
             }
-            if (found)
-                break;
+        }
+        const u32x4 v = h4[qf];
+        const uint32_t cq[4] = {v.x, v.y, v.z, v.w};
+        uint32_t bin = (uint32_t)(lo_b + 4 * qf);
+        found = false;
+#pragma unroll
+        for (int i = 3; i >= 0; i--) {
+            if (!found) {
+                if (bef + cq[i] >= need) {
+                    bin = (uint32_t)(lo_b + 4 * qf + i);
+                    found = true;
+                } else {
+                    bef += cq[i];
+                }
+            }
         }
         bs->bin = bin;
         bs->before = bef;
@@ -610,13 +621,20 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         }
         sl = lo;
     }
+    // the run usually stays inside one slice: keep that slice's bounds in
+    // registers and touch LDS again only when the run crosses into the next
     int src_off[kFinRun];
+    int sl_lo = (int)pre[sl];
+    int sl_hi = sl + 1 < P ? (int)pre[sl + 1] : m; // first candidate of the next slice
 #pragma unroll
     for (int j = 0; j < kFinRun; j++) {
         const int i = min(i0 + min(j, max(n_own - 1, 0)), m - 1);
-        while (sl + 1 < P && pre[sl + 1] <= (uint32_t)i)
+        while (i >= sl_hi) {
             sl++;
-        src_off[j] = sl * kSelSlice + (i - (int)pre[sl]);
+            sl_lo = sl_hi;
+            sl_hi = sl + 1 < P ? (int)pre[sl + 1] : m;
+        }
+        src_off[j] = sl * kSelSlice + (i - sl_lo);
     }
     const u32x2 *src = cand + (int64_t)r * stride;
     uint32_t kk[kFinRun], id[kFinRun];
@@ -711,6 +729,7 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         for (int j = 0; j < kFinRun; j++) {
             if (inbin & (1u << j)) {
                 uint32_t rank = 0;
+#pragma unroll 8
                 for (uint32_t i = 0; i < nl; i++) {
                     const u32x2 y = list[i];
                     rank += (y.x > kk[j] || (y.x == kk[j] && y.y < id[j])) ? 1u : 0u;
