@@ -31,8 +31,8 @@ constexpr int kAttHeads = 64;
 // row starts 256-byte aligned.
 inline int score_stride(const LaunchShape &ls) { return (ls.max_len + 63) / 64 * 64; }
 
-// Index-score pass geometry: 256-token tiles, each workgroup walks a run of
-// tiles of one sequence (about 512 workgroups in all, 1..64 tiles each).
+// Index-score pass geometry: 256-token tiles, each workgroup walks every
+// W-th tile of one sequence (about 512 workgroups in all).
 constexpr int kIdxTile = 256;
 inline int index_tiles_per_seq(const LaunchShape &ls) { return (ls.max_len + kIdxTile - 1) / kIdxTile; }
 inline int index_tiles_per_wg(const LaunchShape &ls)

@@ -16,16 +16,19 @@
 //    logit scale and the output) and parked in one of two LDS tiles,
 //    token-major, in padded rows that keep the operand reads below free of
 //    bank conflicts. Two barriers per step.
-//  - QK + softmax, split by heads: wave w computes S^T[token, head] for
-//    heads 16w..16w+15 on 16x16x32 bf16 MFMA, the tile as A and the query
+//  - QK + softmax, split by heads: scoring wave w computes S^T[token, head]
+//    for heads 16w..16w+15 on 16x16x32 bf16 MFMA, the tile as A and the query
 //    (staged in LDS once per workgroup) as B. Online
 //    softmax in fp32 (log2 domain, exp2, fixed-order reductions, lazy
 //    rescale). The bf16 probabilities go to a small LDS buffer laid out in
 //    the PV operand's k order (one 16-byte write, one 16-byte read).
-//  - PV, split by latent columns: wave w accumulates O[all 64 heads,
-//    columns 128w..128w+127] on 16x16x32 bf16 MFMA, P as A, the tile as B
-//    through LDS transpose loads (ds_read_tr16_b64). Each wave thus reads a
-//    quarter of the tile instead of all of it.
+//  - PV, split by latent columns: each of the 8 waves accumulates O[all 64
+//    heads, its 64 columns] on 16x16x32 bf16 MFMA, P as A, the tile as B
+//    through LDS transpose loads (ds_read_tr16_b64). Each wave thus reads an
+//    eighth of the tile instead of all of it.
+//  - Roles: waves 0-3 score (QK + softmax) while waves 4-7 dequantise and
+//    stage the next tile and keep the gathers in flight; all 8 run PV. Two
+//    waves per SIMD, so one role's waits hide behind the other's work.
 //  - A row with one chunk writes its bf16 output directly. Otherwise every
 //    chunk writes (m, l, O) partials and k_mla_merge folds them in chunk
 //    order 0, 1, 2, ... with the same fp32 formula for every row.
@@ -34,10 +37,12 @@
 
 namespace dsa {
 
-constexpr int kAttThreads = 256;
+constexpr int kAttThreads = 512; // 8 waves, two per SIMD
 constexpr int kStep = 32;            // tokens per LDS tile
 constexpr int kLat = 512;            // latent width
 constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 latent row (64)
+constexpr int kPvCols = kLat / (kAttThreads / kWave); // latent columns of one wave's PV (64)
+constexpr int kPvTiles = kPvCols / 16;                // its 16-column MFMA tiles (4)
 // LDS tile rows (a token's bf16 latent) are padded from 1024 to 1072 bytes
 // (67 chunks). With a 48-byte pad, 16 consecutive rows read at one chunk
 // start 12 words apart modulo the 64 banks (all distinct 4-word groups), and
@@ -83,8 +88,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int nch = (n + kAttChunk - 1) / kAttChunk;
     const int h0 = hg * kAttHeads;              // first head of the group
     const int nh = min(kAttHeads, H - h0);      // heads of the group that exist
-    const int hq = h0 + wave * 16 + n16;        // this lane's head in QK
-    const bool qk_active = wave * 16 < nh;      // the wave's QK heads exist
+    const int hq = h0 + (wave & 3) * 16 + n16;  // this lane's head in QK (waves 0-3)
+    const bool qk_active = wave < 4 && wave * 16 < nh; // a scoring wave whose heads exist
+    const bool producer = wave >= 4;            // waves 4-7 gather and stage the tiles
 
     if (n == 0) {
         if (c == 0) {
@@ -134,16 +140,17 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 
     float m_run = kNegInf; // reference max of the log2-domain logits (head hq)
     float l_run = 0.0f;    // this lane's share of sum exp2(z - m_run)
-    floatx4 o[4][8];       // O[head 16*mt + 4g + v][column 128*wave + 16*nt + n16]
+    floatx4 o[4][kPvTiles]; // O[head 16*mt + 4g + v][column kPvCols*wave + 16*nt + n16]
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-        for (int nt = 0; nt < 8; nt++)
+        for (int nt = 0; nt < kPvTiles; nt++)
             o[mt][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     int mt_count = (nh + 15) / 16; // head tiles that exist
 
-    const int tq = tid >> 5; // staging: tokens 4*tq .. 4*tq+3
-    const int dc = tid & 31; //          latent bytes 16*dc .. 16*dc+15
+    const int ptid = tid - 4 * kWave; // staging thread among waves 4-7
+    const int tq = (ptid >> 5) & 7;   // staging: tokens 4*tq .. 4*tq+3
+    const int dc = ptid & 31;         //          latent bytes 16*dc .. 16*dc+15
 
     // One step's 32 FP8 rows into registers; two steps stay in flight.
     auto gather = [&](u32x4 (&raw)[4], int step) {
@@ -246,18 +253,19 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         *(u32x4 *)(pbuf + (wave * 16 + n16) * kPRowBytes + 16 * g) = pw;
     };
 
-    // PV of step `step` (tile b): O[heads, this wave's 128 columns]. P as A
-    // (k-slot j <-> token 16(j>>2) + 4g + (j&3)), the tile as B through two
+    // PV of step `step` (tile b): O[heads, this wave's kPvCols columns]. P as
+    // A (k-slot j <-> token 16(j>>2) + 4g + (j&3)), the tile as B through two
     // transpose loads of 4 consecutive rows each: lane n16 receives column
-    // 128*wave + 16*nt + n16, rows 4g..4g+3 and 16+4g..16+4g+3.
+    // kPvCols*wave + 16*nt + n16, rows 4g..4g+3 and 16+4g..16+4g+3.
     auto pv = [&](int step, int b) {
         const bool resc = resc_step == step;
         const char *tb = (const char *)tile[b];
-        const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3) + 256 * wave;
+        const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3) +
+                         2 * kPvCols * wave;
         const char *p1 = p0 + 16 * (kRowStride * 16);
-        shortx8 vb[8];
+        shortx8 vb[kPvTiles];
 #pragma unroll
-        for (int nt = 0; nt < 8; nt++) {
+        for (int nt = 0; nt < kPvTiles; nt++) {
             const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p0 + 32 * nt));
             const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p1 + 32 * nt));
             vb[nt] = shortx8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 if (resc) {
                     const floatx4 av = *(const floatx4 *)(alds + 16 * mt + 4 * g);
 #pragma unroll
-                    for (int nt = 0; nt < 8; nt++) {
+                    for (int nt = 0; nt < kPvTiles; nt++) {
                         o[mt][nt][0] *= av[0];
                         o[mt][nt][1] *= av[1];
                         o[mt][nt][2] *= av[2];
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                     }
                 }
 #pragma unroll
-                for (int nt = 0; nt < 8; nt++)
+                for (int nt = 0; nt < kPvTiles; nt++)
                     o[mt][nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, vb[nt]), o[mt][nt]);
             }
         }
@@ -285,19 +293,22 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 
     __syncthreads(); // rowidx and resc_step visible
     u32x4 ra[4], rb[4];
-    gather(ra, 0);
-    if (nsteps > 1)
-        gather(rb, 1);
-    stage(ra, 0);
-    if (nsteps > 2)
-        gather(ra, 2);
-    // step i computes from tile i & 1; during step i the next step's rows
-    // are staged into the other tile and the rows of step i + 3 are gathered
+    if (producer) {
+        gather(ra, 0);
+        if (nsteps > 1)
+            gather(rb, 1);
+        stage(ra, 0);
+        if (nsteps > 2)
+            gather(ra, 2);
+    }
+    // step i computes from tile i & 1; while waves 0-3 score step i, waves
+    // 4-7 stage step i + 1 into the other tile and gather the rows of step
+    // i + 3; then all eight waves run PV of step i
     for (int i = 0; i < nsteps; i += 2) {
         __syncthreads(); // tile 0 holds step i; PV of step i - 1 is done
         if (qk_active)
             qk_softmax(i, 0);
-        if (i + 1 < nsteps) {
+        if (producer && i + 1 < nsteps) {
             stage(rb, 1);
             if (i + 3 < nsteps)
                 gather(rb, i + 3);
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         __syncthreads(); // tile 1 holds step i + 1; PV of step i is done
         if (qk_active)
             qk_softmax(i + 1, 1);
-        if (i + 2 < nsteps) {
+        if (producer && i + 2 < nsteps) {
             stage(ra, 0);
             if (i + 4 < nsteps)
                 gather(ra, i + 4);
@@ -337,9 +348,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 if (h < H) {
                     const float lh = mlds[hl].y;
                     const float inv = lh > 0.0f ? kv_scale / lh : 0.0f;
-                    uint16_t *orow = out + ((int64_t)r * H + h) * kLat + 128 * wave + n16;
+                    uint16_t *orow = out + ((int64_t)r * H + h) * kLat + kPvCols * wave + n16;
 #pragma unroll
-                    for (int nt = 0; nt < 8; nt++)
+                    for (int nt = 0; nt < kPvTiles; nt++)
                         orow[16 * nt] = f32_to_bf16_rne(o[mt][nt][v] * inv);
                 }
             }
@@ -354,9 +365,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 break;
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                float *prow = part_o + (pbase + 16 * mt + 4 * g + v) * kLat + 128 * wave + n16;
+                float *prow = part_o + (pbase + 16 * mt + 4 * g + v) * kLat + kPvCols * wave + n16;
 #pragma unroll
-                for (int nt = 0; nt < 8; nt++)
+                for (int nt = 0; nt < kPvTiles; nt++)
                     prow[16 * nt] = o[mt][nt][v];
             }
         }
