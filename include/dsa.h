@@ -68,7 +68,10 @@ extern "C" {
  */
 typedef struct dsa_shape {
     int32_t num_seqs;           /* S >= 1                                          */
-    int32_t rows_per_seq;       /* K in [1, 8]: 1 = decode, 2..8 = K-token verify  */
+    int32_t rows_per_seq;       /* K in [1, 16]: 1 = decode, 2..8 = K-token        */
+                                /* verify, up to 16 = a row group of one sequence  */
+                                /* scored together (layer.rs: the prefill          */
+                                /* row-group selector, groups of up to 16 rows)    */
     int32_t num_heads;          /* H in [1, 128], attention heads (one KV head)    */
     int32_t latent_dim;         /* kv_lora_rank; must be 512                       */
     int32_t index_heads;        /* Hi in [1, 32]                                   */

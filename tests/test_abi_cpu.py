@@ -39,13 +39,14 @@ def test_workspace_bytes_grows_with_rows_and_refuses_bad_shapes():
     b = dsa.workspace_bytes(good_shape(num_seqs=4))
     assert a > 0 and b > a and a % 256 == 0
     assert dsa.workspace_bytes(good_shape(latent_dim=256)) == 0
-    assert dsa.workspace_bytes(good_shape(rows_per_seq=9)) == 0
+    assert dsa.workspace_bytes(good_shape(rows_per_seq=17)) == 0
+    assert dsa.workspace_bytes(good_shape(rows_per_seq=16)) > 0
     assert dsa.workspace_bytes(good_shape(max_blocks_per_seq=10)) == 0
 
 
 @pytest.mark.parametrize("field,value,code", [
     ("num_seqs", 0, dsa.DSA_EINVAL),
-    ("rows_per_seq", 9, dsa.DSA_EUNSUPPORTED),
+    ("rows_per_seq", 17, dsa.DSA_EUNSUPPORTED),
     ("latent_dim", 576, dsa.DSA_EUNSUPPORTED),
     ("num_heads", 129, dsa.DSA_EUNSUPPORTED),
     ("index_heads", 33, dsa.DSA_EUNSUPPORTED),

@@ -53,6 +53,24 @@ def test_verify_rows_bit_identical_to_serial_calls(K, seed):
     assert_serial_equals_batched(inputs)
 
 
+def test_row_group_of_sixteen_is_bit_identical_and_in_parity():
+    """A row group of 16 rows of one sequence (the prefill row-group shape):
+    every row's scores, selection over its own horizon and output equal a
+    single-row call, and the group agrees with the oracle."""
+    from gpu_common import check_attention, check_scores, check_selection, host
+    inputs = small(num_seqs=2, rows_per_seq=16, lengths="verify", base=3000, top_k=512,
+                   seed=120, page_size=32)
+    assert_serial_equals_batched(inputs)
+    step = dsa.DeviceStep(inputs)
+    step.decode_k()
+    torch.cuda.synchronize()
+    scores, sel, out = host(step)
+    rows = [0, 7, 15, 16, 31]
+    check_scores(inputs, scores, rows)
+    check_selection(inputs, scores, sel, rows)
+    check_attention(inputs, sel, out, rows)
+
+
 def test_verify_rows_bit_identical_when_rows_select_everything():
     # lengths straddle top_k: some rows select all tokens, others run the radix
     inputs = small(num_seqs=2, rows_per_seq=4, lengths="verify", base=2046, top_k=2048,
