@@ -59,6 +59,17 @@ def _load() -> ctypes.CDLL:
     lib.oracle_softmax_weights.argtypes = [i32, i32, i32, i32, i32, P, P, i64, i32, P, i64, P,
                                            P, i64, dbl, dbl, P]
     lib.oracle_softmax_weights.restype = i32
+    lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3fn_encode.restype = ctypes.c_uint8
+    lib.oracle_bf16_encode.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_encode.restype = ctypes.c_uint16
+    lib.oracle_latent_row.argtypes = [i32, P, P, ctypes.c_double, ctypes.c_double, P, P]
+    lib.oracle_latent_row.restype = i32
+    lib.oracle_layernorm_row.argtypes = [i32, P, P, P, ctypes.c_double, P, P]
+    lib.oracle_layernorm_row.restype = i32
+    lib.oracle_cache_write.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, i64, i64, i64,
+                                       i64, ctypes.c_double, ctypes.c_double, P, P]
+    lib.oracle_cache_write.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -170,6 +181,68 @@ def softmax_weights(q, kv_cache, block_tables, seq_lens, sel, kv_scale: float,
                                         float(sm_scale), _p(p))
     _check(rc, "oracle_softmax_weights")
     return p[:n]
+
+
+def e4m3_encode(y: float) -> int:
+    return int(_load().oracle_e4m3fn_encode(float(y)))
+
+
+def bf16_encode(y: float) -> int:
+    return int(_load().oracle_bf16_encode(float(y)))
+
+
+def _bf16_values(a) -> np.ndarray:
+    """bf16 codes (uint16) to float64 by the definition (the upper half of an fp32)."""
+    a = np.asarray(a, dtype=np.uint16)
+    f = (a.astype(np.uint32) << 16).view(np.float32)
+    return f.astype(np.float64)
+
+
+def latent_row(x, w, eps: float, kv_scale: float):
+    """(y float64 [n], codes uint8 [n]) of one latent row; x, w real values."""
+    x = _c(x, np.float64)
+    w = _c(w, np.float64)
+    y = np.empty_like(x)
+    code = np.empty(x.shape[0], dtype=np.uint8)
+    _check(_load().oracle_latent_row(x.shape[0], _p(x), _p(w), eps, 1.0 / kv_scale, _p(y),
+                                     _p(code)), "oracle_latent_row")
+    return y, code
+
+
+def layernorm_row(x, w, b, eps: float):
+    """(y float64 [n], bf16 codes uint16 [n]) of one indexer key row."""
+    x = _c(x, np.float64)
+    w = _c(w, np.float64)
+    b = _c(b, np.float64)
+    y = np.empty_like(x)
+    code = np.empty(x.shape[0], dtype=np.uint16)
+    _check(_load().oracle_layernorm_row(x.shape[0], _p(x), _p(w), _p(b), eps, _p(y), _p(code)),
+           "oracle_layernorm_row")
+    return y, code
+
+
+def cache_write(kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables, rows_per_seq: int,
+                page_size: int, eps: float, kv_scale: float, kv_cache, k_normed):
+    """The cache-write step on copies of the caches. kv_a [R,Dl], latent_w [Dl],
+    k_proj [R,D], k_w [D], k_b [D] are bf16 codes; kv_cache [pages,ps,Dl] uint8;
+    k_normed [S,cap,D] bf16 codes. Returns (kv_cache', k_normed')."""
+    kv = _c(_bf16_values(kv_a), np.float64)
+    lw = _c(_bf16_values(latent_w), np.float64)
+    kp = _c(_bf16_values(k_proj), np.float64)
+    kw = _c(_bf16_values(k_w), np.float64)
+    kb = _c(_bf16_values(k_b), np.float64)
+    seq_lens = _c(seq_lens, np.int32)
+    bt = _c(block_tables, np.int32)
+    cache = np.array(kv_cache, dtype=np.uint8, copy=True, order="C")
+    keys = np.array(k_normed, dtype=np.uint16, copy=True, order="C")
+    R, Dl = kv.shape
+    D = kp.shape[1]
+    rc = _load().oracle_cache_write(R, rows_per_seq, Dl, D, _p(kv), _p(lw), _p(kp), _p(kw),
+                                    _p(kb), _p(seq_lens), _p(bt), bt.shape[1], page_size,
+                                    cache.shape[0], keys.shape[1], eps, kv_scale, _p(cache),
+                                    _p(keys))
+    _check(rc, "oracle_cache_write")
+    return cache, keys
 
 
 def decode(inputs: dict, rows=None):

@@ -45,6 +45,10 @@
  * the K rows of a sequence share its key cache and its block table ([P1]
  * `decode_k`, the A65 note on the block-table row stride of zero).
  *
+ * Beside the path, the oracle also covers the cache-write side that feeds it
+ * (latent RMSNorm + FP8 encode + paged slot write, and the indexer key
+ * LayerNorm row; see the last section).
+ *
  * Parity status of each function is stated at its definition.
  */
 #include <math.h>
@@ -364,6 +368,154 @@ int oracle_softmax_weights(int K, int H, int Dl, int r, int h,
     for (int64_t j = 0; j < n; j++)
         p[j] = exp(p[j] - zmax) / denom;
     return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The cache-write side: the step that feeds the path's two caches.        */
+/* ------------------------------------------------------------------------ */
+
+/* Round-to-nearest-even encoding of a real value into OCP E4M3 (FN) with
+ * saturation to +-448 (the synthetic-cache encoding reading of the pages:
+ * the write scales by 1/kv_scale and stores FP8; nearest-even with
+ * saturation is taken where the pages are silent). Written from the format
+ * definition above: the non-negative finite codes 0x00..0x7E are the
+ * magnitudes in increasing order, subnormal codes 0..7 step 2^-9, then each
+ * binade 2^(e-7) * [1, 2) in eight steps, so a rounded step count n in a
+ * binade maps to code (binade base code + n) with a carry into the next
+ * binade when n reaches 8. The sign goes to bit 7 (also for -0.0). y must
+ * not be NaN. Pinned by brute force against the decoded table. */
+uint8_t oracle_e4m3fn_encode(double y)
+{
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs(y);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) /* subnormal binade: steps of 2^-9 */
+        return sign | (uint8_t)nearbyint(ldexp(a, 9));
+    int E;
+    const double f = frexp(a, &E); /* a = f * 2^E, f in [0.5, 1) */
+    const int ue = E - 1;          /* a = (2f) * 2^ue, 2f in [1, 2) */
+    const double n = nearbyint((2.0 * f - 1.0) * 8.0);
+    return sign | (uint8_t)(((ue + 7) << 3) + (int)n);
+}
+
+/* Round-to-nearest-even encoding of a real value into bfloat16 (8-bit
+ * exponent with bias 127, 7 stored mantissa bits); the same construction as
+ * the E4M3 encoder with 128 steps per binade. Finite, non-NaN inputs inside
+ * the normal range are all this oracle produces. Pinned against torch. */
+uint16_t oracle_bf16_encode(double y)
+{
+    const uint16_t sign = signbit(y) ? 0x8000 : 0x0000;
+    const double a = fabs(y);
+    if (a == 0.0)
+        return sign;
+    int E;
+    const double f = frexp(a, &E);
+    const int ue = E - 1;
+    if (ue < -126) /* subnormal: steps of 2^-133 */
+        return sign | (uint16_t)nearbyint(ldexp(a, 133));
+    const double n = nearbyint((2.0 * f - 1.0) * 128.0);
+    const int code = ((ue + 127) << 7) + (int)n;
+    return sign | (uint16_t)(code >= 0x7F80 ? 0x7F80 : code);
+}
+
+/* One latent row for the paged FP8 cache ([P1] module header, first trap:
+ * the plain RMSNorm x * rms * w with rms = 1 / sqrt(mean(x^2) + eps), not
+ * the 1 + w form; the `latent_write` kernel handle doc: RMSNorm, then FP8,
+ * then the paged slot write; doc of the `kv_scale` field: the write takes
+ * 1 / kv_scale). y[i] is the real value before encoding, code[i] its E4M3
+ * byte. */
+int oracle_latent_row(int n, const double *x, const double *w, double eps, double inv_kv_scale,
+                      double *y, uint8_t *code)
+{
+    if (n < 1)
+        return ORACLE_EINVAL;
+    double ss = 0.0;
+    for (int i = 0; i < n; i++)
+        ss += x[i] * x[i];
+    const double rms = 1.0 / sqrt(ss / (double)n + eps);
+    for (int i = 0; i < n; i++) {
+        y[i] = x[i] * rms * w[i] * inv_kv_scale;
+        if (isnan(y[i]))
+            return ORACLE_ENAN;
+        code[i] = oracle_e4m3fn_encode(y[i]);
+    }
+    return ORACLE_OK;
+}
+
+/* One indexer key row ([P1] module header, second trap: `indexer.k_norm` is
+ * a LayerNorm with a bias -- mean subtraction, then the affine with weight
+ * and bias; `indexer_forward`: the launch passes the layer's rms_eps):
+ *   y = (x - mean) / sqrt(var + eps) * w + b,  var the population variance.
+ * code[i] is the bfloat16 the key cache stores. */
+int oracle_layernorm_row(int n, const double *x, const double *w, const double *b, double eps,
+                         double *y, uint16_t *code)
+{
+    if (n < 1)
+        return ORACLE_EINVAL;
+    double mean = 0.0;
+    for (int i = 0; i < n; i++)
+        mean += x[i];
+    mean /= (double)n;
+    double var = 0.0;
+    for (int i = 0; i < n; i++)
+        var += (x[i] - mean) * (x[i] - mean);
+    var /= (double)n;
+    const double inv = 1.0 / sqrt(var + eps);
+    for (int i = 0; i < n; i++) {
+        y[i] = (x[i] - mean) * inv * w[i] + b[i];
+        if (isnan(y[i]))
+            return ORACLE_ENAN;
+        code[i] = oracle_bf16_encode(y[i]);
+    }
+    return ORACLE_OK;
+}
+
+/* The whole write for R = S * K rows: row r (sequence s = r / K) stores its
+ * token at position pos = seq_lens[r] - 1 ([P1] `decode_k`: the length
+ * handed on is the position plus one):
+ *   kv_cache[page * page_size + pos % page_size] = latent row of kv_a[r]
+ *     with page = block_tables[s][pos / page_size]  ([P1] `decode_k` slot
+ *     computation), skipped when page is outside [0, num_pages);
+ *   k_normed[s][pos] = key row of k_proj[r]  ([P1] `indexer_forward`).
+ * Rows with seq_lens[r] < 1 or pos >= k_capacity write nothing. The caches
+ * are updated in place (the caller passes copies). Inputs are the decoded
+ * values of the bf16 operands. */
+int oracle_cache_write(int R, int K, int Dl, int D, const double *kv_a, const double *latent_w,
+                       const double *k_proj, const double *k_w, const double *k_b,
+                       const int32_t *seq_lens, const int32_t *block_tables, int64_t max_blocks,
+                       int64_t page_size, int64_t num_pages, int64_t k_capacity, double eps,
+                       double kv_scale, uint8_t *kv_cache, uint16_t *k_normed)
+{
+    if (R < 1 || K < 1 || Dl < 1 || D < 1 || page_size < 1 || !(kv_scale > 0.0))
+        return ORACLE_EINVAL;
+    double *y = (double *)malloc(sizeof(double) * (size_t)(Dl > D ? Dl : D));
+    uint8_t *c8 = (uint8_t *)malloc((size_t)Dl);
+    uint16_t *c16 = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)D);
+    int rc = ORACLE_OK;
+    for (int r = 0; r < R && rc == ORACLE_OK; r++) {
+        const int s = r / K;
+        const int64_t pos = (int64_t)seq_lens[r] - 1;
+        if (pos < 0 || pos >= k_capacity)
+            continue;
+        rc = oracle_layernorm_row(D, k_proj + (int64_t)r * D, k_w, k_b, eps, y, c16);
+        if (rc != ORACLE_OK)
+            break;
+        memcpy(k_normed + ((int64_t)s * k_capacity + pos) * D, c16, sizeof(uint16_t) * (size_t)D);
+        if (pos / page_size >= max_blocks)
+            continue;
+        const int32_t page = block_tables[(int64_t)s * max_blocks + pos / page_size];
+        if (page < 0 || page >= num_pages)
+            continue;
+        rc = oracle_latent_row(Dl, kv_a + (int64_t)r * Dl, latent_w, eps, 1.0 / kv_scale, y, c8);
+        if (rc != ORACLE_OK)
+            break;
+        memcpy(kv_cache + ((int64_t)page * page_size + pos % page_size) * Dl, c8, (size_t)Dl);
+    }
+    free(y);
+    free(c8);
+    free(c16);
+    return rc;
 }
 
 /* Number of threads the parallel loops above use. */

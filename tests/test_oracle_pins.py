@@ -306,3 +306,115 @@ def test_attend_empty_row_is_zero_and_bad_ids_are_refused():
     with pytest.raises(oracle.OracleError):
         oracle.mla_decode(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"],
                           np.array([[0, 1, 2, 9]], np.int32), x["kv_scale"], x["sm_scale"])
+
+
+# ---------------------------------------------------------------------------
+# The cache-write side (latent RMSNorm + FP8 write, indexer key LayerNorm).
+
+def brute_force_e4m3(y, table):
+    """Nearest finite E4M3 code to y by exhaustive search, ties to the even
+    code (mantissa LSB 0), saturating beyond +-448."""
+    finite = [c for c in range(256) if not math.isnan(table[c])]
+    best = None
+    for c in finite:
+        if (c & 0x80) != (0x80 if math.copysign(1.0, y) < 0 else 0):
+            continue
+        d = abs(table[c] - y)
+        if best is None or d < best[0] - 1e-300 or (abs(d - best[0]) <= 1e-300 and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_e4m3_encoder_is_the_nearest_code_ties_to_even():
+    table = torch_e4m3_table()
+    rng = np.random.default_rng(7)
+    ys = list(rng.standard_normal(300) * 40.0) + list(rng.standard_normal(100) * 0.01)
+    pos = sorted(v for v in table[:0x7F] if not math.isnan(v))
+    # every midpoint between neighbouring magnitudes, and its neighbours
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        ys += [mid, -mid, math.nextafter(mid, 0.0), math.nextafter(mid, 1e9)]
+    ys += [0.0, -0.0, 448.0, 447.9, 460.0, 1e6, -1e6, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11]
+    for y in ys:
+        assert oracle.e4m3_encode(y) == brute_force_e4m3(y, table), y
+
+
+def test_e4m3_encoder_agrees_with_torch_cast_on_float32_values():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(4000) * 30.0).astype(np.float32)
+    x = np.clip(x, -448.0, 448.0)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_encoder_agrees_with_torch_cast_on_float32_values():
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(4000) * 3.0, rng.standard_normal(100) * 1e-30,
+                        [0.0, -0.0, 1.0, -2.5, 65504.0]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_encode(float(v)) for v in x], dtype=np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_latent_row_rms_is_one_and_scale_free():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal(512) * 3.0
+    ones = np.ones(512)
+    y, _ = oracle.latent_row(x, ones, eps=0.0, kv_scale=1.0)
+    assert abs(np.mean(y * y) - 1.0) < 1e-12            # RMSNorm output has unit RMS
+    y2, c2 = oracle.latent_row(x * 7.5, ones, eps=0.0, kv_scale=1.0)
+    _, c1 = oracle.latent_row(x, ones, eps=0.0, kv_scale=1.0)
+    np.testing.assert_array_equal(c1, c2)                # invariant to a positive scale
+    w = rng.uniform(0.5, 1.5, 512)
+    yw, _ = oracle.latent_row(x, w, eps=0.0, kv_scale=0.5)
+    np.testing.assert_allclose(yw, y * w / 0.5, rtol=1e-13)  # plain weight (no 1 + w), 1/kv_scale
+    # eps enters under the root: mean(x^2) + eps
+    ye, _ = oracle.latent_row(x, ones, eps=0.25, kv_scale=1.0)
+    np.testing.assert_allclose(ye, x / math.sqrt(np.mean(x * x) + 0.25), rtol=1e-13)
+
+
+def test_layernorm_row_is_standardised_then_affine():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(128) * 2.0 + 5.0
+    y, _ = oracle.layernorm_row(x, np.ones(128), np.zeros(128), eps=0.0)
+    assert abs(np.mean(y)) < 1e-12 and abs(np.mean(y * y) - 1.0) < 1e-12
+    y_shift, _ = oracle.layernorm_row(x + 100.0, np.ones(128), np.zeros(128), eps=0.0)
+    np.testing.assert_allclose(y_shift, y, atol=1e-12)   # mean subtraction
+    w = rng.uniform(0.5, 1.5, 128)
+    b = rng.standard_normal(128) * 0.1
+    ya, codes = oracle.layernorm_row(x, w, b, eps=0.0)
+    np.testing.assert_allclose(ya, y * w + b, rtol=1e-12, atol=1e-15)  # weight and BIAS
+    ref = torch.from_numpy(ya.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+    # the stored code is the bf16 of the value (equal to the float32 route
+    # except where the float32 rounding lands exactly on a bf16 midpoint)
+    assert (codes == ref.numpy().view(np.uint16)).mean() > 0.99
+
+
+def test_cache_write_slot_arithmetic_and_untouched_elsewhere():
+    """A hand-worked placement: page size 4, block table row [3, 0, 2]; the
+    token at position 5 lands in logical block 1 -> physical page 0, slot 1."""
+    Dl, D, ps = 8, 4, 4
+    rng = np.random.default_rng(12)
+    kv_a = bf16(rng.standard_normal((2, Dl)))
+    k_proj = bf16(rng.standard_normal((2, D)))
+    lw = bf16(np.ones(Dl))
+    kw = bf16(np.ones(D))
+    kb = bf16(np.zeros(D))
+    bt = np.array([[3, 0, 2], [1, -1, -1]], np.int32)
+    cache = np.full((4, ps, Dl), 0x55, np.uint8)
+    keys = np.full((2, 12, D), 0x1234, np.uint16)
+    seq_lens = np.array([6, 0], np.int32)                   # row 1 writes nothing
+    c2, k2 = oracle.cache_write(kv_a, lw, k_proj, kw, kb, seq_lens, bt, 1, ps, 1e-6, 0.5,
+                                cache, keys)
+    changed = np.argwhere((c2 != cache).any(axis=2))
+    assert changed.tolist() == [[0, 1]]                      # page 0, slot 1 only
+    _, codes = oracle.latent_row(oracle._bf16_values(kv_a[0]), np.ones(Dl), 1e-6, 0.5)
+    np.testing.assert_array_equal(c2[0, 1], codes)
+    assert np.argwhere((k2 != keys).any(axis=2)).tolist() == [[0, 5]]
+    # an unmapped page is skipped for the latent but the key row is stored
+    c3, k3 = oracle.cache_write(kv_a, lw, k_proj, kw, kb, np.array([6, 2], np.int32),
+                                np.array([[3, 0, 2], [-1, -1, -1]], np.int32), 1, ps, 1e-6, 0.5,
+                                cache, keys)
+    assert np.argwhere((c3 != cache).any(axis=2)).tolist() == [[0, 1]]
+    assert np.argwhere((k3 != keys).any(axis=2)).tolist() == [[0, 5], [1, 1]]
