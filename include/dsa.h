@@ -2,7 +2,8 @@
  * dsa.h -- C ABI of the MI355X (gfx950) DSA decode hot path.
  *
  * The path has three steps, each one entry point, plus one entry point that
- * runs all three for every row of a call:
+ * runs all three for every row of a call (and, beside them, the cache write
+ * that feeds the path, dsa_cache_write):
  *
  *   dsa_index_scores  lightning-indexer score of every cached token
  *   dsa_topk_select   exact per-row top-k over [0, L_r)
@@ -181,6 +182,34 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w,
                  const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
                  float sm_scale, float *scores, int32_t *sel, void *out, void *ws,
                  size_t ws_bytes, void *stream);
+
+/*
+ * The cache-write side that feeds the path (the step before it): row r
+ * stores its token at pos = seq_lens[r] - 1 in both caches.
+ *   latent: the plain RMSNorm y = x * w / sqrt(mean(x^2) + eps) of kv_a[r]
+ *     (layer.rs module header, first trap: the vanilla form, no 1 + w),
+ *     times 1 / kv_scale (the `kv_scale` field: the write takes 1/scale),
+ *     saturated to +-448, encoded to OCP E4M3 with round-to-nearest-even and
+ *     written to kv_cache[page * page_size + pos % page_size] with page =
+ *     block_tables[s][pos / page_size] (the `latent_write` kernel handle;
+ *     `decode_k` slot arithmetic). A page outside [0, num_pages) skips it.
+ *   key: the LayerNorm with bias y = (x - mean) / sqrt(var + eps) * k_w +
+ *     k_b of k_proj[r] (module header, second trap), var the population
+ *     variance, stored as bf16 (nearest-even) at k_normed[s][pos]
+ *     (`indexer_forward`).
+ * Norm sums run in fp32. Rows with seq_lens[r] outside [1, max_len] write
+ * nothing; two rows of one sequence must not name the same position.
+ *   kv_a     [R, latent_dim] bf16     latent_w [latent_dim] bf16
+ *   k_proj   [R, index_dim] bf16      k_w, k_b [index_dim] bf16
+ *   seq_lens [R] int32                block_tables [S, max_blocks_per_seq] int32
+ *   kv_cache [num_pages, page_size, latent_dim] E4M3 bytes (updated in place)
+ *   k_normed [S, k_capacity, index_dim] bf16 (updated in place)
+ * eps >= 0 and finite; kv_scale > 0 and finite.
+ */
+int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent_w,
+                    const void *k_proj, const void *k_w, const void *k_b,
+                    const int32_t *seq_lens, const int32_t *block_tables, float eps,
+                    float kv_scale, uint8_t *kv_cache, void *k_normed, void *stream);
 
 /*
  * Row stride, in floats, of every scores buffer for `shape`: max_len rounded

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_abi.hip", "index_scores.hip", "topk_select.hip", "mla_decode.hip"]
+SOURCES = ["dsa_abi.hip", "index_scores.hip", "topk_select.hip", "mla_decode.hip",
+           "cache_write.hip"]
 ARCH = "gfx950"
 
 COMMON = [

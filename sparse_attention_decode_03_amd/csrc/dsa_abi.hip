@@ -265,4 +265,32 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, cons
     return DSA_OK;
 }
 
+int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent_w,
+                    const void *k_proj, const void *k_w, const void *k_b,
+                    const int32_t *seq_lens, const int32_t *block_tables, float eps,
+                    float kv_scale, uint8_t *kv_cache, void *k_normed, void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if ((rc = check_ptr(kv_a, "kv_a")) || (rc = check_ptr(latent_w, "latent_w")) ||
+        (rc = check_ptr(k_proj, "k_proj")) || (rc = check_ptr(k_w, "k_w")) ||
+        (rc = check_ptr(k_b, "k_b")) || (rc = check_ptr(seq_lens, "seq_lens")) ||
+        (rc = check_ptr(block_tables, "block_tables")) || (rc = check_ptr(kv_cache, "kv_cache")) ||
+        (rc = check_ptr(k_normed, "k_normed")))
+        return rc;
+    if (!(eps >= 0.0f) || eps == __builtin_huge_valf())
+        return fail(DSA_EINVAL, "eps must be finite and non-negative");
+    if (!(kv_scale > 0.0f) || kv_scale == __builtin_huge_valf())
+        return fail(DSA_EINVAL, "kv_scale must be positive and finite");
+    return launched(dsa::launch_cache_write(ls, (const uint16_t *)kv_a, (const uint16_t *)latent_w,
+                                            (const uint16_t *)k_proj, (const uint16_t *)k_w,
+                                            (const uint16_t *)k_b, seq_lens, block_tables, eps,
+                                            kv_scale, kv_cache, (uint16_t *)k_normed,
+                                            (hipStream_t)stream),
+                    "cache_write");
+}
+
 } // extern "C"

@@ -76,6 +76,10 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
                   hipStream_t stream);
+int launch_cache_write(const LaunchShape &ls, const uint16_t *kv_a, const uint16_t *latent_w,
+                       const uint16_t *k_proj, const uint16_t *k_w, const uint16_t *k_b,
+                       const int32_t *seq_lens, const int32_t *block_tables, float eps,
+                       float kv_scale, uint8_t *kv_cache, uint16_t *k_normed, hipStream_t stream);
 int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
                       float kv_scale, float sm_scale, uint16_t *out, char *ws,

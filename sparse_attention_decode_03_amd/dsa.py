@@ -29,6 +29,7 @@ EXPORTS = (
     "dsa_topk_select",
     "dsa_mla_decode",
     "dsa_decode_k",
+    "dsa_cache_write",
     "dsa_score_stride",
     "dsa_bt_entries_needed",
     "dsa_last_error",
@@ -104,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_mla_decode.restype = i32
     lib.dsa_decode_k.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P, sz, P]
     lib.dsa_decode_k.restype = i32
+    lib.dsa_cache_write.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P]
+    lib.dsa_cache_write.restype = i32
     lib.dsa_score_stride.argtypes = [S]
     lib.dsa_score_stride.restype = sz
     lib.dsa_bt_entries_needed.argtypes = [sz, sz, sz]
@@ -182,6 +185,13 @@ def decode_k(shape: Shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_le
                                _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), kv_scale,
                                sm_scale, _ptr(scores), _ptr(sel), _ptr(out), _ptr(ws), nb,
                                _stream(stream)))
+
+
+def cache_write(shape: Shape, kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables,
+                eps: float, kv_scale: float, kv_cache, k_normed, stream=None) -> None:
+    _check(load().dsa_cache_write(ctypes.byref(shape), _ptr(kv_a), _ptr(latent_w), _ptr(k_proj),
+                                  _ptr(k_w), _ptr(k_b), _ptr(seq_lens), _ptr(block_tables), eps,
+                                  kv_scale, _ptr(kv_cache), _ptr(k_normed), _stream(stream)))
 
 
 class DeviceStep:
