@@ -102,6 +102,51 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     if (ONE_ROW)
         load_row(s);
 
+    // One 32-token block of row r: MFMA over D, ReLU-weighted head sum, the
+    // score store and (GM) the group maxima of the block.
+    auto score_block = [&](int r, int L, int t0, int col0, const bf16x8 (&kb)[KS]) {
+        floatx16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            acc = mfma32x32x16(qa[ks], kb[ks], acc);
+        float part = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+            part = __builtin_fmaf(wv[v], __builtin_fmaxf(acc[v], 0.0f), part);
+        const float tot = part + __shfl_xor(part, 32, kWave);
+        const int t = t0 + col0 + (lane & 31);
+        if (hl == 0 && t < L)
+            scores[(int64_t)r * stride + t] = tot;
+        if (GM) {
+            // groups are aligned: a quad of lanes holds a 4-token group,
+            // lanes 0..31 the 32-token group
+            uint32_t k = t < L ? score_key(tot) : 0u;
+            k = max(k, dpp_u32<kDppQuadXor1>(k));
+            k = max(k, dpp_u32<kDppQuadXor2>(k));
+            if (hl == 0 && (lane & 3) == 0 && t < L)
+                gm4[(int64_t)r * (stride / 4) + (t >> 2)] = k;
+            k = max(k, dpp_u32<kDppRowHalfMirror>(k));
+            k = max(k, dpp_u32<kDppRowMirror>(k)); // every lane: its row's max
+            const uint32_t k32 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 0),
+                                     (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
+            if (lane == 0 && t < L)
+                gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k32;
+        }
+    };
+
+    // Several rows (K > 1): the tile's K x 8 (row, block) items are split
+    // into four contiguous ranges, one per wave, in row-major order, so a
+    // wave keeps one row's query across blocks (with K = 4 each wave owns
+    // one row for the whole run and loads its query once).
+    constexpr int kBlocks = kIdxTile / 32;
+    const int items = K * kBlocks / (kIdxThreads / kWave);
+    const int item0 = wave * items;
+    int loaded = -1;
+    if (!ONE_ROW && item0 / kBlocks == (item0 + items - 1) / kBlocks) {
+        loaded = item0 / kBlocks;
+        load_row(s * K + loaded);
+    }
+
     load_tile(tile_first);
     for (int tile = tile_first; tile < tile_end; tile += W) {
         const int t0 = tile * kIdxTile;
@@ -117,54 +162,44 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         if (tile + W < tile_end)
             load_tile(tile + W); // in flight while this tile computes
 
-        // key operands: column (token) lane%32, k-chunks hl*KS + ks
-        bf16x8 kb[2][KS];
-#pragma unroll
-        for (int b = 0; b < 2; b++) {
-            const int row = wave * 64 + b * 32 + (lane & 31);
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                const int c = hl * KS + ks;
-                kb[b][ks] = as_bf16x8(lds[row * CH + (c ^ (row & (CH - 1)))]);
-            }
-        }
-
-        for (int j = 0; j < K; j++) {
-            const int r = s * K + j;
-            const int L = min(max(seq_lens[r], 0), max_len);
-            if (t0 >= L)
-                continue;
-            if (!ONE_ROW)
-                load_row(r);
+        if (ONE_ROW) {
+            // key operands: column (token) lane%32, k-chunks hl*KS + ks
+            bf16x8 kb[2][KS];
 #pragma unroll
             for (int b = 0; b < 2; b++) {
-                floatx16 acc = {};
+                const int row = wave * 64 + b * 32 + (lane & 31);
 #pragma unroll
-                for (int ks = 0; ks < KS; ks++)
-                    acc = mfma32x32x16(qa[ks], kb[b][ks], acc);
-                float part = 0.0f;
-#pragma unroll
-                for (int v = 0; v < 16; v++)
-                    part = __builtin_fmaf(wv[v], __builtin_fmaxf(acc[v], 0.0f), part);
-                const float tot = part + __shfl_xor(part, 32, kWave);
-                const int t = t0 + wave * 64 + b * 32 + (lane & 31);
-                if (hl == 0 && t < L)
-                    scores[(int64_t)r * stride + t] = tot;
-                if (GM) {
-                    // groups are aligned: a quad of lanes holds a 4-token
-                    // group, lanes 0..31 the 32-token group
-                    uint32_t k = t < L ? score_key(tot) : 0u;
-                    k = max(k, dpp_u32<kDppQuadXor1>(k));
-                    k = max(k, dpp_u32<kDppQuadXor2>(k));
-                    if (hl == 0 && (lane & 3) == 0 && t < L)
-                        gm4[(int64_t)r * (stride / 4) + (t >> 2)] = k;
-                    k = max(k, dpp_u32<kDppRowHalfMirror>(k));
-                    k = max(k, dpp_u32<kDppRowMirror>(k)); // every lane: its row's max
-                    const uint32_t k32 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 0),
-                                             (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
-                    if (lane == 0 && t < L)
-                        gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k32;
+                for (int ks = 0; ks < KS; ks++) {
+                    const int c = hl * KS + ks;
+                    kb[b][ks] = as_bf16x8(lds[row * CH + (c ^ (row & (CH - 1)))]);
                 }
+            }
+            const int L = min(max(seq_lens[s], 0), max_len);
+#pragma unroll
+            for (int b = 0; b < 2; b++)
+                score_block(s, L, t0, wave * 64 + b * 32, kb[b]);
+        } else {
+            // the wave's (row, 32-token block) items, rows of one item range
+            // reuse the loaded query
+            for (int it = item0; it < item0 + items; it++) {
+                const int j = it / kBlocks;
+                const int blk = it % kBlocks;
+                const int r = s * K + j;
+                const int L = min(max(seq_lens[r], 0), max_len);
+                if (t0 + blk * 32 >= L)
+                    continue;
+                if (j != loaded) {
+                    load_row(r);
+                    loaded = j;
+                }
+                bf16x8 kb[KS];
+                const int row = blk * 32 + (lane & 31);
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const int c = hl * KS + ks;
+                    kb[ks] = as_bf16x8(lds[row * CH + (c ^ (row & (CH - 1)))]);
+                }
+                score_block(r, L, t0, blk * 32, kb);
             }
         }
     }
