@@ -130,7 +130,7 @@ Workspace workspace_layout(const LaunchShape &ls)
     if (nch > 1) {
         off = align256(off + R * hgc * nch * kAttHeads * 2 * sizeof(float));
         w.part_o = off;
-        off = align256(off + R * hgc * nch * kAttHeads * 512 * sizeof(float));
+        off = align256(off + R * hgc * nch * kAttHeads * 512 * sizeof(uint16_t)); // bf16 O
     }
     w.total = off;
     return w;

@@ -61,7 +61,7 @@ struct Workspace {
     size_t cnt;     // [R][sel_slices] candidates per slice
     size_t gm4;     // [R][score_stride / 4] max key of each 4-token group
     size_t gm32;    // [R][score_stride / 32] max key of each 32-token group
-    size_t part_o, part_ml;
+    size_t part_o, part_ml; // per-chunk attention partials: bf16 O, fp32 (m, l)
     size_t total;
 };
 Workspace workspace_layout(const LaunchShape &ls);

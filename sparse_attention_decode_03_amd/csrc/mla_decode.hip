@@ -30,8 +30,10 @@
 //    stage the next tile and keep the gathers in flight; all 8 run PV. Two
 //    waves per SIMD, so one role's waits hide behind the other's work.
 //  - A row with one chunk writes its bf16 output directly. Otherwise every
-//    chunk writes (m, l, O) partials and k_mla_merge folds them in chunk
-//    order 0, 1, 2, ... with the same fp32 formula for every row.
+//    chunk writes (m, l) in fp32 and its unnormalised O rounded to bf16 (the
+//    precision of the output; half the partial traffic), and k_mla_merge
+//    folds them in chunk order 0, 1, 2, ... with the same fp32 formula for
+//    every row.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -62,7 +64,7 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
     const int32_t *__restrict__ bt, const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ sel, float *__restrict__ part_o, float2 *__restrict__ part_ml,
+    const int32_t *__restrict__ sel, uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml,
     uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
@@ -368,17 +370,17 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 break;
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                float *prow = part_o + (pbase + 16 * mt + 4 * g + v) * kLat + kPvCols * wave + n16;
+                uint16_t *prow = part_o + (pbase + 16 * mt + 4 * g + v) * kLat + kPvCols * wave + n16;
 #pragma unroll
                 for (int nt = 0; nt < kPvTiles; nt++)
-                    prow[16 * nt] = o[mt][nt][v];
+                    prow[16 * nt] = f32_to_bf16_rne(o[mt][nt][v]);
             }
         }
     }
 }
 
 // Fold the per-chunk partials of every (row, head) in chunk order.
-__global__ __launch_bounds__(128) void k_mla_merge(const float *__restrict__ part_o,
+__global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ part_o,
                                                    const float2 *__restrict__ part_ml,
                                                    const int32_t *__restrict__ seq_lens,
                                                    uint16_t *__restrict__ out, int H, int top_k,
@@ -410,7 +412,9 @@ __global__ __launch_bounds__(128) void k_mla_merge(const float *__restrict__ par
             const int64_t pi =
                 (((int64_t)r * hg_count + hg) * nch_max + min(c0 + k, nch - 1)) * kAttHeads + hl;
             ml[k] = part_ml[pi];
-            ov[k] = *(const floatx4 *)(part_o + pi * kLat + d);
+            const u32x2 pk = *(const u32x2 *)(part_o + pi * kLat + d);
+            ov[k] = floatx4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
+                            __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)};
         }
 #pragma unroll
         for (int k = 0; k < kB; k++) {
@@ -443,7 +447,7 @@ int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *k
     const int nch_max = att_chunks(ls) > 0 ? att_chunks(ls) : 1;
     const int hgc = att_head_groups(ls);
     const float qk_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634074);
-    float *part_o = (float *)(ws + wl.part_o);
+    uint16_t *part_o = (uint16_t *)(ws + wl.part_o);
     float2 *part_ml = (float2 *)(ws + wl.part_ml);
     hipLaunchKernelGGL(k_mla_decode, dim3(nch_max * hgc, ls.num_rows), dim3(kAttThreads), 0,
                        stream, q, kv_cache, block_tables, seq_lens, sel, part_o, part_ml, out,
