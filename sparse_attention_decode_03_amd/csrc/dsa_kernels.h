@@ -31,21 +31,10 @@ constexpr int kAttHeads = 64;
 // row starts 256-byte aligned.
 inline int score_stride(const LaunchShape &ls) { return (ls.max_len + 63) / 64 * 64; }
 
-// Index-score pass geometry: 256-token tiles, each workgroup walks every
-// W-th tile of one sequence (about 512 workgroups in all).
+// Index-score pass geometry: 256-token tiles (the balance of tiles over
+// workgroups is computed on the device from the lengths).
 constexpr int kIdxTile = 256;
-inline int index_tiles_per_seq(const LaunchShape &ls) { return (ls.max_len + kIdxTile - 1) / kIdxTile; }
-inline int index_tiles_per_wg(const LaunchShape &ls)
-{
-    const long total = (long)index_tiles_per_seq(ls) * ls.num_seqs;
-    int tpw = (int)((total + 511) / 512);
-    return tpw < 1 ? 1 : (tpw > 64 ? 64 : tpw);
-}
-inline int index_wgs_per_seq(const LaunchShape &ls)
-{
-    const int tpw = index_tiles_per_wg(ls);
-    return (index_tiles_per_seq(ls) + tpw - 1) / tpw;
-}
+
 inline int att_chunks(const LaunchShape &ls)
 {
     const int n = ls.top_k < ls.max_len ? ls.top_k : ls.max_len;

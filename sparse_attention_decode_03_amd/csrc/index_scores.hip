@@ -27,6 +27,7 @@
 namespace dsa {
 
 constexpr int kIdxThreads = 256; // 4 waves x 64 tokens of a tile
+constexpr int kIdxWgTarget = 512; // workgroups the tiles of a call spread over
 
 // LDS: the key tile, 256 tokens x 16 chunks of 16 bytes (64 KiB at D = 128).
 
@@ -34,8 +35,8 @@ template <int D, bool ONE_ROW, bool GM>
 __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint16_t *__restrict__ k_normed, const int32_t *__restrict__ seq_lens,
-    float *__restrict__ scores, uint32_t *__restrict__ gm4, uint32_t *__restrict__ gm32, int K,
-    int Hi, int64_t cap, int max_len, int stride)
+    float *__restrict__ scores, uint32_t *__restrict__ gm4, uint32_t *__restrict__ gm32, int S,
+    int K, int Hi, int64_t cap, int max_len, int stride)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per key row
     constexpr int KS = D / 16; // MFMA k-steps
@@ -46,7 +47,55 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const int lane = tid % kWave;
     const int wave = tid / kWave;
     const int hl = lane / 32;
-    const int s = blockIdx.y;
+
+    // ---- balance the tiles of all sequences over about kIdxWgTarget
+    // workgroups from the device-side lengths: every workgroup computes the
+    // same split (tiles per workgroup from the total), sequence s gets
+    // ceil(tiles_s / tpw) workgroups, and this workgroup claims its sequence
+    // and slot from a prefix of those counts ----
+    __shared__ uint32_t bscan[kIdxThreads / kWave + 1];
+    __shared__ int claim[3];
+    auto seq_tiles = [&](int sq) {
+        int lm = 0;
+        for (int j = 0; j < K; j++)
+            lm = max(lm, min(max(seq_lens[sq * K + j], 0), max_len));
+        return (lm + kIdxTile - 1) / kIdxTile;
+    };
+    const int per = (S + kIdxThreads - 1) / kIdxThreads; // sequences per thread
+    const int sq0 = min(tid * per, S), sq1 = min(sq0 + per, S);
+    uint32_t my_tiles = 0;
+    for (int sq = sq0; sq < sq1; sq++)
+        my_tiles += (uint32_t)seq_tiles(sq);
+    uint32_t total_tiles;
+    (void)block_exclusive_scan<kIdxThreads>(my_tiles, bscan, &total_tiles);
+    const uint32_t tpw = max(1u, (total_tiles + kIdxWgTarget - 1) / kIdxWgTarget);
+    uint32_t my_wgs = 0;
+    for (int sq = sq0; sq < sq1; sq++)
+        my_wgs += ((uint32_t)seq_tiles(sq) + tpw - 1) / tpw;
+    uint32_t total_wgs;
+    uint32_t wg_base = block_exclusive_scan<kIdxThreads>(my_wgs, bscan, &total_wgs);
+    if (tid == 0)
+        claim[0] = -1;
+    __syncthreads();
+    const uint32_t me = blockIdx.x;
+    if (me >= wg_base && me < wg_base + my_wgs) { // exactly one thread
+        uint32_t at = wg_base;
+        for (int sq = sq0; sq < sq1; sq++) {
+            const int nt = seq_tiles(sq);
+            const uint32_t w_s = ((uint32_t)nt + tpw - 1) / tpw;
+            if (me < at + w_s) {
+                claim[0] = sq;
+                claim[1] = (int)(me - at);
+                claim[2] = (int)w_s;
+                break;
+            }
+            at += w_s;
+        }
+    }
+    __syncthreads();
+    if (claim[0] < 0)
+        return; // past the last workgroup this split needs
+    const int s = claim[0];
 
     int lmax = 0;
     for (int j = 0; j < K; j++)
@@ -54,8 +103,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     // tiles interleave across the sequence's workgroups (workgroup x takes
     // tiles x, x + W, x + 2W, ...), so at any moment the workgroups stream
     // neighbouring 64 KiB blocks and spread over every HBM channel
-    const int W = gridDim.x;
-    const int tile_first = blockIdx.x;
+    const int W = claim[2];
+    const int tile_first = claim[1];
     const int tile_end = (lmax + kIdxTile - 1) / kIdxTile;
     if (tile_first >= tile_end)
         return;
@@ -211,7 +260,8 @@ static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, 
                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
 {
     hipLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM>), grid, dim3(kIdxThreads), 0, stream,
-                       q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.rows_per_seq,
+                       q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.num_seqs,
+                       ls.rows_per_seq,
                        ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls));
 }
 
@@ -240,11 +290,12 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
                         uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
 {
-    // About 512 workgroups in all; each walks every W-th tile of one
-    // sequence with the next tile's loads in flight.
+    // About kIdxWgTarget workgroups in all, balanced over the sequences by
+    // their device-side lengths; each walks every W-th tile of one sequence
+    // with the next tile's loads in flight.
     if ((gm4 == nullptr) != (gm32 == nullptr))
         return -1;
-    dim3 grid(index_wgs_per_seq(ls), ls.num_seqs);
+    dim3 grid(kIdxWgTarget + ls.num_seqs); // enough for any split of the tiles
     if (ls.index_dim == 128)
         launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream);
     else if (ls.index_dim == 64)
