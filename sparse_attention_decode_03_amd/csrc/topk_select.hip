@@ -363,7 +363,7 @@ __device__ __forceinline__ uint32_t spread8(uint32_t x)
     return x;
 }
 
-__device__ void select_row_full(const float *__restrict__ scores, int r, int L, int32_t *out,
+__device__ __noinline__ void select_row_full(const float *__restrict__ scores, int r, int L, int32_t *out,
                                 u32x2 *rspill, uint32_t *gbitmap_row, int stride, int top_k,
                                 uint32_t (*hsub)[kHistBins], u32x2 *cbuf, uint32_t *lbitmap,
                                 BinSearch *bs, uint32_t *ccount)
