@@ -9,26 +9,25 @@
 // Decomposition (a function of the row alone, never of R, so every row is
 // bit-reproducible whichever rows share a launch):
 //  - A row's selection is cut into chunks of kAttChunk slots. One workgroup
-//    of 4 waves covers one chunk for 64 heads. It walks the chunk in steps of
-//    32 tokens: each token's 512-byte FP8 row is gathered through the block
-//    table with coalesced 16-byte loads (two steps ahead), dequantised
-//    exactly to bf16 (E4M3 is a subset of bf16; kv_scale is folded into the
-//    logit scale and the output) and parked in one of two LDS tiles,
-//    token-major, in padded rows that keep the operand reads below free of
-//    bank conflicts. Two barriers per step.
-//  - QK + softmax, split by heads: scoring wave w computes S^T[token, head]
-//    for heads 16w..16w+15 on 16x16x32 bf16 MFMA, the tile as A and the query
-//    (staged in LDS once per workgroup) as B. Online
+//    of 8 waves covers one chunk for 64 heads, in steps of 32 tokens. Each
+//    token's 512-byte FP8 row is gathered through the block table with
+//    coalesced 16-byte loads, dequantised exactly to bf16 (E4M3 is a subset
+//    of bf16; kv_scale is folded into the logit scale and the output) and
+//    parked token-major in one of three LDS tiles, in padded rows that keep
+//    the operand reads below free of bank conflicts.
+//  - Two roles, one barrier per step. Waves 0-3 score: wave w holds the
+//    query of heads 16w..16w+15 in registers and computes S^T[token, head]
+//    on 16x16x32 bf16 MFMA (the tile as A, the query as B), then the online
 //    softmax in fp32 (log2 domain, exp2, fixed-order reductions, lazy
-//    rescale). The bf16 probabilities go to a small LDS buffer laid out in
-//    the PV operand's k order (one 16-byte write, one 16-byte read).
-//  - PV, split by latent columns: each of the 8 waves accumulates O[all 64
-//    heads, its 64 columns] on 16x16x32 bf16 MFMA, P as A, the tile as B
-//    through LDS transpose loads (ds_read_tr16_b64). Each wave thus reads an
-//    eighth of the tile instead of all of it.
-//  - Roles: waves 0-3 score (QK + softmax) while waves 4-7 dequantise and
-//    stage the next tile and keep the gathers in flight; all 8 run PV. Two
-//    waves per SIMD, so one role's waits hide behind the other's work.
+//    rescale); the bf16 probabilities go to a small LDS buffer in the PV
+//    operand's k order. Waves 4-7 accumulate: wave v holds O[64 heads,
+//    latent columns 128v..128v+127] and runs PV on 16x16x32 bf16 MFMA (P as
+//    A, the tile as B through LDS transpose loads, ds_read_tr16_b64); they
+//    also dequantise and stage the tiles and keep the gathers in flight.
+//    While the scoring waves work on step i + 1, the accumulating waves run
+//    PV of step i and stage step i + 2, so the matrix cores of every SIMD
+//    see both products at once. Each result element is still produced by
+//    the same operations in the same order, step after step.
 //  - A row with one chunk writes its bf16 output directly. Otherwise every
 //    chunk writes (m, l) in fp32 and its unnormalised O rounded to bf16 (the
 //    precision of the output; half the partial traffic), and k_mla_merge
@@ -39,12 +38,14 @@
 
 namespace dsa {
 
-constexpr int kAttThreads = 512; // 8 waves, two per SIMD
+constexpr int kAttThreads = 512;  // 8 waves, two per SIMD: one scoring, one accumulating
 constexpr int kStep = 32;            // tokens per LDS tile
+constexpr int kTiles = 3;            // tiles in LDS: scored, accumulated, being staged
 constexpr int kLat = 512;            // latent width
 constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 latent row (64)
-constexpr int kPvCols = kLat / (kAttThreads / kWave); // latent columns of one wave's PV (64)
-constexpr int kPvTiles = kPvCols / 16;                // its 16-column MFMA tiles (4)
+constexpr int kPvCols = kLat / 4;    // latent columns of one accumulating wave (128)
+constexpr int kPvTiles = kPvCols / 16; // its 16-column MFMA tiles (8)
+constexpr int kMaxSteps = kAttChunk / kStep;
 // LDS tile rows (a token's bf16 latent) are padded from 1024 to 1056 bytes
 // (66 chunks): measured on gfx950 the fastest stride for the QK operand
 // reads (16 rows at one 16-byte column per lane group), and within 10 % of
@@ -68,13 +69,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
-    __shared__ u32x4 tile[2][kStep * kRowStride];        // bf16 tokens x latent, padded rows
-    __shared__ u32x4 qlds[kAttHeads * kRowStride];       // bf16 query of the 64 heads, padded
-    __shared__ __align__(16) uint8_t pbuf[kAttHeads * kPRowBytes]; // bf16 P, PV k order
-    __shared__ float alds[kAttHeads];                    // per-head rescale factors
+    __shared__ u32x4 tile[kTiles][kStep * kRowStride];   // bf16 tokens x latent, padded rows
+    __shared__ __align__(16) uint8_t pbuf[2][kAttHeads * kPRowBytes]; // bf16 P, PV k order
+    __shared__ __align__(16) float alds[2][kAttHeads];   // per-head rescale factors
     __shared__ float2 mlds[kAttHeads];                   // per-head (m, l) at the end
     __shared__ int rowidx[kAttChunk];                    // latent row of each slot, -1 = skip
-    __shared__ int resc_step;                            // last step whose O needs a rescale
+    __shared__ int resc[kMaxSteps];                      // step s: O needs its alphas
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -88,11 +88,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int L = min(max(seq_lens[r], 0), max_len);
     const int n = min(top_k, L);
     const int nch = (n + kAttChunk - 1) / kAttChunk;
-    const int h0 = hg * kAttHeads;              // first head of the group
-    const int nh = min(kAttHeads, H - h0);      // heads of the group that exist
-    const int hq = h0 + (wave & 3) * 16 + n16;  // this lane's head in QK (waves 0-3)
-    const bool qk_active = wave < 4 && wave * 16 < nh; // a scoring wave whose heads exist
-    const bool producer = wave >= 4;            // waves 4-7 gather and stage the tiles
+    const int h0 = hg * kAttHeads;         // first head of the group
+    const int nh = min(kAttHeads, H - h0); // heads of the group that exist
+    const int mt_count = (nh + 15) / 16;   // 16-head tiles that exist
 
     if (n == 0) {
         if (c == 0) {
@@ -123,151 +121,213 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         }
         rowidx[k] = row;
     }
-    if (tid == 0)
-        resc_step = -1;
+    if (tid < kMaxSteps)
+        resc[tid] = 0;
+    // P rows of heads that no scoring wave covers stay zero
+    for (int i = tid; i < 2 * kAttHeads * kPRowBytes / 16; i += kAttThreads)
+        ((u32x4 *)pbuf)[i] = u32x4{0u, 0u, 0u, 0u};
 
-    // ---- query of the group's 64 heads into LDS (padded head rows);
-    // branch-free, a missing head loads head H-1 and is zeroed ----
+    if (wave < 4) {
+        // ================= scoring waves: QK + online softmax =================
+        const int hl = wave * 16 + n16; // this lane's head within the group
+        const bool active = wave * 16 < nh;
+        // query of head hl, latent dims 32 ks + 8 g .. +7 (the B operand);
+        // branch-free, a missing head loads head H-1 and is zeroed
+        u32x4 qr[16];
+        {
+            const uint16_t *qrow = q + ((int64_t)r * H + min(h0 + hl, H - 1)) * kLat + 8 * g;
 #pragma unroll
-    for (int i = 0; i < kAttHeads * kRowChunks / kAttThreads; i++) {
-        const int id = i * kAttThreads + tid;
-        const int hh = id / kRowChunks;
-        const int ch = id % kRowChunks;
-        const int h = h0 + hh;
-        u32x4 v = *(const u32x4 *)(q + ((int64_t)r * H + min(h, H - 1)) * kLat + ch * 8);
-        if (h >= H)
-            v = u32x4{0u, 0u, 0u, 0u};
-        qlds[hh * kRowStride + ch] = v;
+            for (int ks = 0; ks < 16; ks++) {
+                qr[ks] = *(const u32x4 *)(qrow + 32 * ks);
+                if (h0 + hl >= H)
+                    qr[ks] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        float m_run = kNegInf; // reference max of the log2-domain logits (head hl)
+        float l_run = 0.0f;    // this lane's share of sum exp2(z - m_run)
+
+        // QK and online softmax of one step; leaves P and the alphas in
+        // buffer step & 1 and marks the step when a reference moved
+        auto qk_softmax = [&](int step) {
+            const u32x4 *tb = tile[step % kTiles];
+            floatx4 sacc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+            // A: tile rows n16 and 16 + n16, k = latent dims 32 ks + 8 g .. +7.
+            // Software-pipelined in groups of four k-steps: the operands of
+            // group k0 + 1 are requested before the products of group k0, so
+            // the LDS latency hides behind the matrix core.
+            const u32x4 *t0row = tb + n16 * kRowStride + g;
+            const u32x4 *t1row = tb + (16 + n16) * kRowStride + g;
+            u32x4 a[2][8];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                a[0][2 * j] = t0row[4 * j];
+                a[0][2 * j + 1] = t1row[4 * j];
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < 4; k0++) {
+                if (k0 + 1 < 4) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        a[(k0 + 1) & 1][2 * j] = t0row[4 * (4 * (k0 + 1) + j)];
+                        a[(k0 + 1) & 1][2 * j + 1] = t1row[4 * (4 * (k0 + 1) + j)];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    sacc[0] = mfma16x16x32(as_bf16x8(a[k0 & 1][2 * j]), as_bf16x8(qr[4 * k0 + j]), sacc[0]);
+                    sacc[1] = mfma16x16x32(as_bf16x8(a[k0 & 1][2 * j + 1]), as_bf16x8(qr[4 * k0 + j]), sacc[1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // lane: head hl, tokens 16*(j>>2) + 4g + (j&3) for j = 0..7
+            float z[8];
+            float mx = kNegInf;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float v = sacc[j >> 2][j & 3] * qk_log2;
+                z[j] = rowidx[step * kStep + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
+                mx = __builtin_fmaxf(mx, z[j]);
+            }
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            // The reference max moves only when the step's max exceeds it by
+            // more than kRescaleSlack (log2 units): then p <= 2^kRescaleSlack,
+            // so fp32 sums and bf16 probabilities stay well scaled, and O is
+            // rescaled only on rare steps. The rule is a function of the row's
+            // data alone, so results stay bit-reproducible; the partial state
+            // (m_ref, l, O) merges exactly as with the true max.
+            const bool move = mx > m_run + kRescaleSlack;
+            const float m_new = move ? mx : m_run;
+            const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+            const float alpha = exp2f(m_run - m_use);
+            float p[8];
+            float rs = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                p[j] = exp2f(z[j] - m_use);
+                rs += p[j];
+            }
+            l_run = __builtin_fmaf(l_run, alpha, rs);
+            if (g == 0)
+                alds[step & 1][hl] = alpha;
+            if (__ballot(move && m_run != kNegInf) != 0 && lane == 0)
+                resc[step] = 1;
+            m_run = m_new;
+            u32x4 pw;
+            pw.x = pack_bf16x2(p[0], p[1]);
+            pw.y = pack_bf16x2(p[2], p[3]);
+            pw.z = pack_bf16x2(p[4], p[5]);
+            pw.w = pack_bf16x2(p[6], p[7]);
+            *(u32x4 *)(pbuf[step & 1] + hl * kPRowBytes + 16 * g) = pw;
+        };
+
+        __syncthreads(); // rowidx, resc cleared
+        __syncthreads(); // tiles 0 and 1 staged
+        if (active)
+            qk_softmax(0);
+        __syncthreads(); // P of step 0
+        for (int i = 0; i < nsteps; i++) {
+            if (active && i + 1 < nsteps)
+                qk_softmax(i + 1);
+            __syncthreads();
+        }
+        // per-head (m, l): the four lanes of a head hold shares of l
+        const float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+        const float l_all = l_tot + __shfl_xor(l_tot, 32, kWave);
+        if (active && g == 0) {
+            mlds[hl] = float2{m_run, l_all};
+            if (nch > 1) {
+                const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
+                part_ml[pbase + hl] = float2{m_run, l_all};
+            }
+        }
+        __syncthreads(); // mlds
+        return;
     }
 
-    float m_run = kNegInf; // reference max of the log2-domain logits (head hq)
-    float l_run = 0.0f;    // this lane's share of sum exp2(z - m_run)
-    floatx4 o[4][kPvTiles]; // O[head 16*mt + 4g + v][column kPvCols*wave + 16*nt + n16]
+    // ================= accumulating waves: gather, stage, PV =================
+    const int v = wave - 4;
+    const int ptid = tid - 4 * kWave; // 0..255
+    const int tq = ptid >> 5;         // staging: tokens 4 tq .. 4 tq + 3
+    const int dc = ptid & 31;         //          latent bytes 16 dc .. 16 dc + 15
+    floatx4 o[4][kPvTiles]; // O[head 16 mt + n16][columns kPvCols v + 16 nt + 4 g + e]
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
         for (int nt = 0; nt < kPvTiles; nt++)
             o[mt][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    int mt_count = (nh + 15) / 16; // head tiles that exist
 
-    const int ptid = tid - 4 * kWave; // staging thread among waves 4-7
-    const int tq = (ptid >> 5) & 7;   // staging: tokens 4*tq .. 4*tq+3
-    const int dc = ptid & 31;         //          latent bytes 16*dc .. 16*dc+15
-
-    // One step's 32 FP8 rows into registers; two steps stay in flight.
+    // One step's 32 FP8 rows into registers (slot indices first, then the
+    // four loads back to back; a skipped slot reads latent row 0 and is
+    // zeroed when staged, so nothing waits on the loads here).
     auto gather = [&](u32x4 (&raw)[4], int step) {
+        int row[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int k = step * kStep + 4 * tq + i;
-            const int row = (k < kAttChunk) ? rowidx[k] : -1;
-            // branch-free so the four loads issue back to back: a skipped
-            // slot reads latent row 0 and is zeroed
-            raw[i] = *(const u32x4 *)(kv + (int64_t)max(row, 0) * kLat + 16 * dc);
-            if (row < 0)
-                raw[i] = u32x4{0u, 0u, 0u, 0u};
+            row[i] = (k < kAttChunk) ? rowidx[k] : -1;
         }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            raw[i] = *(const u32x4 *)(kv + (int64_t)max(row[i], 0) * kLat + 16 * dc);
     };
-    // Dequantise (exact) into LDS tile b.
-    auto stage = [&](const u32x4 (&raw)[4], int b) {
+    // Dequantise (exact) into the tile of `step`.
+    auto stage = [&](const u32x4 (&raw)[4], int step) {
+        u32x4 *tb = tile[step % kTiles];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = 4 * tq + i;
+            const int k = step * kStep + t;
+            const bool skip = k >= kAttChunk || rowidx[k] < 0;
+            const u32x4 w = skip ? u32x4{0u, 0u, 0u, 0u} : raw[i];
             u32x4 lo, hi;
-            lo.x = e4m3x2_to_bf16x2_exact<false>(raw[i].x);
-            lo.y = e4m3x2_to_bf16x2_exact<true>(raw[i].x);
-            lo.z = e4m3x2_to_bf16x2_exact<false>(raw[i].y);
-            lo.w = e4m3x2_to_bf16x2_exact<true>(raw[i].y);
-            hi.x = e4m3x2_to_bf16x2_exact<false>(raw[i].z);
-            hi.y = e4m3x2_to_bf16x2_exact<true>(raw[i].z);
-            hi.z = e4m3x2_to_bf16x2_exact<false>(raw[i].w);
-            hi.w = e4m3x2_to_bf16x2_exact<true>(raw[i].w);
+            lo.x = e4m3x2_to_bf16x2_exact<false>(w.x);
+            lo.y = e4m3x2_to_bf16x2_exact<true>(w.x);
+            lo.z = e4m3x2_to_bf16x2_exact<false>(w.y);
+            lo.w = e4m3x2_to_bf16x2_exact<true>(w.y);
+            hi.x = e4m3x2_to_bf16x2_exact<false>(w.z);
+            hi.y = e4m3x2_to_bf16x2_exact<true>(w.z);
+            hi.z = e4m3x2_to_bf16x2_exact<false>(w.w);
+            hi.w = e4m3x2_to_bf16x2_exact<true>(w.w);
             // lanes dc and dc + 8 would hit the same banks with the chunk
             // pair in order; the upper eight of every sixteen write it swapped
             const int sw = (dc >> 3) & 1;
-            tile[b][t * kRowStride + 2 * dc + sw] = sw ? hi : lo;
-            tile[b][t * kRowStride + 2 * dc + 1 - sw] = sw ? lo : hi;
+            tb[t * kRowStride + 2 * dc + sw] = sw ? hi : lo;
+            tb[t * kRowStride + 2 * dc + 1 - sw] = sw ? lo : hi;
         }
     };
-
-    // QK and online softmax of step `step` (tile b) for this wave's heads;
-    // leaves P in pbuf and, on a step where a reference moved, the alphas.
-    auto qk_softmax = [&](int step, int b) {
-        floatx4 sacc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
-        // A: tile rows n16 and 16 + n16, k = latent dims 32*ks + 8*g .. +7;
-        // B: query of head wave*16 + n16 with the same k order. Operands of
-        // four k-steps are read ahead of their products.
-        const u32x4 *t0row = tile[b] + n16 * kRowStride + g;
-        const u32x4 *t1row = tile[b] + (16 + n16) * kRowStride + g;
-        const u32x4 *qrow = qlds + (wave * 16 + n16) * kRowStride + g;
-#pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) {
-            u32x4 a0[4], a1[4], qb[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                a0[j] = t0row[4 * (k0 + j)];
-                a1[j] = t1row[4 * (k0 + j)];
-                qb[j] = qrow[4 * (k0 + j)];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                sacc[0] = mfma16x16x32(as_bf16x8(a0[j]), as_bf16x8(qb[j]), sacc[0]);
-                sacc[1] = mfma16x16x32(as_bf16x8(a1[j]), as_bf16x8(qb[j]), sacc[1]);
-            }
-        }
-        // lane: head hq, tokens 16*(j>>2) + 4g + (j&3) for j = 0..7
-        float z[8];
-        float mx = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float v = sacc[j >> 2][j & 3] * qk_log2;
-            z[j] = rowidx[step * kStep + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
-            mx = __builtin_fmaxf(mx, z[j]);
-        }
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        // The reference max moves only when the step's max exceeds it by
-        // more than kRescaleSlack (log2 units): then p <= 2^kRescaleSlack, so
-        // fp32 sums and bf16 probabilities stay well scaled, and O is
-        // rescaled only on rare steps. The rule is a function of the row's
-        // data alone, so results stay bit-reproducible; the partial state
-        // (m_ref, l, O) merges exactly as with the true max.
-        const bool move = mx > m_run + kRescaleSlack;
-        const float m_new = move ? mx : m_run;
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        float p[8];
-        float rs = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            p[j] = exp2f(z[j] - m_use);
-            rs += p[j];
-        }
-        l_run = __builtin_fmaf(l_run, alpha, rs);
-        // every step leaves its alphas (1 where nothing moved); the PV waves
-        // apply them only on a step marked here
-        if (g == 0)
-            alds[wave * 16 + n16] = alpha;
-        if (__ballot(move && m_run != kNegInf) != 0 && lane == 0)
-            resc_step = step;
-        m_run = m_new;
-        u32x4 pw;
-        pw.x = pack_bf16x2(p[0], p[1]);
-        pw.y = pack_bf16x2(p[2], p[3]);
-        pw.z = pack_bf16x2(p[4], p[5]);
-        pw.w = pack_bf16x2(p[6], p[7]);
-        *(u32x4 *)(pbuf + (wave * 16 + n16) * kPRowBytes + 16 * g) = pw;
-    };
-
-    // PV of step `step` (tile b): O[heads, this wave's kPvCols columns]. P as
-    // A (k-slot j <-> token 16(j>>2) + 4g + (j&3)), the tile as B through two
-    // transpose loads of 4 consecutive rows each: lane n16 receives column
-    // kPvCols*wave + 16*nt + n16, rows 4g..4g+3 and 16+4g..16+4g+3.
-    auto pv = [&](int step, int b) {
-        const bool resc = resc_step == step;
-        const char *tb = (const char *)tile[b];
+    // PV of one step, transposed: O^T[this wave's columns, heads] += V^T P^T.
+    // The tile as A through two transpose loads of 4 consecutive rows each
+    // (lane n16 receives column kPvCols v + 16 nt + n16, rows 4g..4g+3 and
+    // 16+4g..16+4g+3, i.e. k-slot j <-> token 16(j>>2) + 4g + (j&3)), P as B
+    // in the same k order. A lane ends with 4 consecutive columns of one
+    // head: one rescale factor per head tile, 8-byte output stores.
+    auto pv = [&](int step) {
+        const bool rs = resc[step] != 0;
+        const char *tb = (const char *)tile[step % kTiles];
+        const uint8_t *pb = pbuf[step & 1];
         const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3) +
-                         2 * kPvCols * wave;
+                         2 * kPvCols * v;
         const char *p1 = p0 + 16 * (kRowStride * 16);
+        if (rs) {
+#pragma unroll
+            for (int mt = 0; mt < 4; mt++) {
+                const float a = alds[step & 1][16 * mt + n16];
+#pragma unroll
+                for (int nt = 0; nt < kPvTiles; nt++) {
+                    o[mt][nt][0] *= a;
+                    o[mt][nt][1] *= a;
+                    o[mt][nt][2] *= a;
+                    o[mt][nt][3] *= a;
+                }
+            }
+        }
+        // every operand of the step is requested before the first product
+        bf16x8 pa[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+            pa[mt] = as_bf16x8(*(const u32x4 *)(pb + (16 * mt + n16) * kPRowBytes + 16 * g));
         shortx8 vb[kPvTiles];
 #pragma unroll
         for (int nt = 0; nt < kPvTiles; nt++) {
@@ -275,106 +335,94 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
             const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p1 + 32 * nt));
             vb[nt] = shortx8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-            if (mt < mt_count) {
-                const bf16x8 pa = as_bf16x8(*(const u32x4 *)(pbuf + (16 * mt + n16) * kPRowBytes + 16 * g));
-                if (resc) {
-                    const floatx4 av = *(const floatx4 *)(alds + 16 * mt + 4 * g);
+        for (int nt = 0; nt < kPvTiles; nt++) {
 #pragma unroll
-                    for (int nt = 0; nt < kPvTiles; nt++) {
-                        o[mt][nt][0] *= av[0];
-                        o[mt][nt][1] *= av[1];
-                        o[mt][nt][2] *= av[2];
-                        o[mt][nt][3] *= av[3];
-                    }
-                }
-#pragma unroll
-                for (int nt = 0; nt < kPvTiles; nt++)
-                    o[mt][nt] = mfma16x16x32(pa, __builtin_bit_cast(bf16x8, vb[nt]), o[mt][nt]);
-            }
+            for (int mt = 0; mt < 4; mt++) // head tiles past the group's heads see P = 0
+                o[mt][nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vb[nt]), pa[mt], o[mt][nt]);
         }
     };
 
-    __syncthreads(); // rowidx and resc_step visible
+    __syncthreads(); // rowidx, resc cleared
+    // steps 0 and 1 staged, steps 2 and 3 in flight (ra holds even steps,
+    // rb odd ones; step i + 2 is staged from the buffer step i used)
     u32x4 ra[4], rb[4];
-    if (producer) {
-        gather(ra, 0);
-        if (nsteps > 1)
-            gather(rb, 1);
-        stage(ra, 0);
-        if (nsteps > 2)
-            gather(ra, 2);
-    }
-    // step i computes from tile i & 1; while waves 0-3 score step i, waves
-    // 4-7 stage step i + 1 into the other tile and gather the rows of step
-    // i + 3; then all eight waves run PV of step i
-    for (int i = 0; i < nsteps; i += 2) {
-        __syncthreads(); // tile 0 holds step i; PV of step i - 1 is done
-        if (qk_active)
-            qk_softmax(i, 0);
-        if (producer && i + 1 < nsteps) {
-            stage(rb, 1);
-            if (i + 3 < nsteps)
-                gather(rb, i + 3);
+    gather(ra, 0);
+    if (nsteps > 1)
+        gather(rb, 1);
+    stage(ra, 0);
+    if (nsteps > 2)
+        gather(ra, 2);
+    if (nsteps > 1)
+        stage(rb, 1);
+    if (nsteps > 3)
+        gather(rb, 3);
+    __syncthreads(); // tiles 0 and 1 staged
+    __syncthreads(); // P of step 0
+    // step i: PV of step i and staging of step i + 2, while the scoring
+    // waves score step i + 1
+    for (int i = 0; i < nsteps; i++) {
+        if (i + 2 < nsteps) {
+            if ((i & 1) == 0) {
+                stage(ra, i + 2);
+                if (i + 4 < nsteps)
+                    gather(ra, i + 4);
+            } else {
+                stage(rb, i + 2);
+                if (i + 4 < nsteps)
+                    gather(rb, i + 4);
+            }
         }
-        __syncthreads(); // P of step i visible
-        pv(i, 0);
-        if (i + 1 >= nsteps)
-            break;
-        __syncthreads(); // tile 1 holds step i + 1; PV of step i is done
-        if (qk_active)
-            qk_softmax(i + 1, 1);
-        if (producer && i + 2 < nsteps) {
-            stage(ra, 0);
-            if (i + 4 < nsteps)
-                gather(ra, i + 4);
-        }
+        pv(i);
         __syncthreads();
-        pv(i + 1, 1);
     }
+    __syncthreads(); // mlds
 
-    // ---- per-head (m, l): the four lanes of a head hold shares of l ----
-    const float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-    const float l_all = l_tot + __shfl_xor(l_tot, 32, kWave);
-    if (qk_active && g == 0)
-        mlds[wave * 16 + n16] = float2{m_run, l_all};
-    __syncthreads();
-
-    if (nch == 1) {
+    // Output through LDS: each wave parks its O block (64 heads x its 128
+    // columns, bf16) in its own region of the now idle tiles, then writes it
+    // back as whole 256-byte head rows with 16-byte stores. Only this wave
+    // touches its region, so a wait for its own LDS writes is enough.
+    constexpr int kORowBytes = 2 * kPvCols + 16; // padded: 16 rows at one column spread over the banks
+    static_assert(4 * kAttHeads * kORowBytes <= (int)sizeof(tile), "O blocks fit the tiles");
+    uint8_t *oreg = (uint8_t *)tile + v * (kAttHeads * kORowBytes);
+    const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
+    auto park = [&](auto scale_of) {
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
-            if (mt >= mt_count)
-                break;
+            const int hl = 16 * mt + n16;
+            const float sc = scale_of(hl);
 #pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const int hl = 16 * mt + 4 * g + v;
-                const int h = h0 + hl;
-                if (h < H) {
-                    const float lh = mlds[hl].y;
-                    const float inv = lh > 0.0f ? kv_scale / lh : 0.0f;
-                    uint16_t *orow = out + ((int64_t)r * H + h) * kLat + kPvCols * wave + n16;
-#pragma unroll
-                    for (int nt = 0; nt < kPvTiles; nt++)
-                        orow[16 * nt] = f32_to_bf16_rne(o[mt][nt][v] * inv);
-                }
+            for (int nt = 0; nt < kPvTiles; nt++) {
+                u32x2 pk;
+                pk.x = pack_bf16x2(o[mt][nt][0] * sc, o[mt][nt][1] * sc);
+                pk.y = pack_bf16x2(o[mt][nt][2] * sc, o[mt][nt][3] * sc);
+                *(u32x2 *)(oreg + hl * kORowBytes + 2 * (16 * nt + 4 * g)) = pk;
             }
         }
-    } else {
-        const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
-        if (qk_active && g == 0)
-            part_ml[pbase + wave * 16 + n16] = float2{m_run, l_all};
+    };
+    if (nch == 1) { // the final output: O / l, with kv_scale
+        park([&](int hl) {
+            const float lh = mlds[hl].y;
+            return lh > 0.0f ? kv_scale / lh : 0.0f;
+        });
+    } else {        // a partial: O as accumulated
+        park([](int) { return 1.0f; });
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane: 16 bytes (8 columns) of head row 4 i + (lane >> 4)
+    const int cb = 16 * (lane & 15);
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-            if (mt >= mt_count)
-                break;
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                uint16_t *prow = part_o + (pbase + 16 * mt + 4 * g + v) * kLat + kPvCols * wave + n16;
-#pragma unroll
-                for (int nt = 0; nt < kPvTiles; nt++)
-                    prow[16 * nt] = f32_to_bf16_rne(o[mt][nt][v]);
-            }
+    for (int i = 0; i < kAttHeads / 4; i++) {
+        const int hl = 4 * i + (lane >> 4);
+        const int h = h0 + hl;
+        const u32x4 val = *(const u32x4 *)(oreg + hl * kORowBytes + cb);
+        if (hl < nh) {
+            uint16_t *orow = (nch == 1) ? out + ((int64_t)r * H + h) * kLat
+                                        : part_o + (pbase + hl) * kLat;
+            *(u32x4 *)((uint8_t *)(orow + kPvCols * v) + cb) = val;
         }
     }
 }

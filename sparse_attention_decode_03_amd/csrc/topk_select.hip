@@ -59,6 +59,7 @@ struct BinSearch {
     uint32_t red[2][kRowWaves];
     uint32_t bin;
     uint32_t before;
+    uint32_t total; // count of the last histogram walked by find_bin_desc_wave0
 };
 
 // Over the LDS histogram h[0..nbins), walked from the highest bin down
@@ -124,8 +125,8 @@ __device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
 }
 
 // Descending walk over the kSelBins-bin LDS histogram h (16-byte aligned):
-// the bin where the running count first reaches `need`, and the count of
-// everything above it, into bs. Run by wave 0 alone (64 bins per lane, one
+// the bin where the running count first reaches `need`, the count of
+// everything above it and the histogram's total, into bs. Run by wave 0 alone (64 bins per lane, one
 // DPP lane scan); a barrier of the caller publishes the result. An
 // inconsistent histogram (total < need) yields bin 0.
 __device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t need,
@@ -149,6 +150,8 @@ __device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t 
         bs->bin = 0u;
         bs->before = 0u;
     }
+    if (lane == kWave - 1)
+        bs->total = x;
     if (run < need && x >= need) { // exactly one lane: its quads downwards in
         uint32_t bef = run;        // registers, then the one quad from LDS
         int qf = 0;
@@ -554,8 +557,135 @@ __device__ __noinline__ void select_row_full(const float *__restrict__ scores, i
 }
 
 // ---------------------------------------------------------------------------
+// Exact cut and output, shared by the finishing and the whole-row
+// workgroups. The kFinThreads threads hold the row's candidates, N each,
+// thread-major in ascending token order (bit j of `valid` marks a held
+// candidate), with every candidate key in [lo, hi]. Relative 12-bit digits
+// narrow a key window to the bin holding the top_k-th candidate; the bin's
+// members are then ranked directly under (key desc, index asc), and the
+// selected ids leave in ascending order. Needs the first histogram (the
+// area's first kSelBins words) cleared and ccount zero, both published by a
+// barrier. Returns false, having written nothing, when fewer than top_k
+// candidates are held (the same answer in every thread).
+template <int N>
+__device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const uint32_t (&id)[N],
+                                                uint32_t valid, uint32_t lo, uint32_t hi,
+                                                int top_k, int32_t *out, uint8_t *area,
+                                                BinSearch &bs, uint32_t &ccount)
+{
+    static_assert(N <= 32, "one mask bit per held candidate");
+    const int tid = threadIdx.x;
+    uint32_t *hist0 = (uint32_t *)area;                   // two histograms,
+    uint32_t *hist1 = (uint32_t *)(area + kSelBins * 4);  // then the member list
+    u32x2 *list = (u32x2 *)(area + 2 * kSelBins * 4);
+    uint32_t base = lo;
+    int bits = bit_len(hi - lo); // window [base, base + 2^bits) holds every key
+    uint32_t need = (uint32_t)top_k;
+    uint32_t bin_lo = base;      // the boundary bin [bin_lo, bin_lo + 2^shift)
+    int shift = 0;
+    uint32_t count_b = 0u;
+    uint32_t *h = hist0, *hn = hist1;
+    bool first = true;
+    while (true) {
+        shift = max(bits - kSelDigit, 0);
+#pragma unroll
+        for (int j = 0; j < N; j++) {
+            if ((valid & (1u << j)) && kk[j] >= base) {
+                const uint32_t d = (kk[j] - base) >> shift;
+                if (d < (uint32_t)kSelBins)
+                    atomicAdd(&h[d], 1u);
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < kSelBins; i += kFinThreads)
+            hn[i] = 0u;
+        if (tid < kWave)
+            find_bin_desc_wave0(h, need, &bs);
+        __syncthreads();
+        if (first && bs.total < (uint32_t)top_k)
+            return false; // the first window holds every candidate
+        first = false;
+        const uint32_t b = bs.bin;
+        need -= bs.before;           // members of bin b to take
+        count_b = h[b];
+        bin_lo = base + (b << shift);
+        if (count_b <= (uint32_t)kRankList || shift == 0)
+            break;
+        base = bin_lo;
+        bits = shift;
+        uint32_t *t = h;
+        h = hn;
+        hn = t;
+        __syncthreads(); // everyone has read h[b] before it is cleared again
+    }
+    // keys >= bin_lo + 2^shift are taken, keys < bin_lo are not; the bin's
+    // members take `need` places
+    uint32_t take = 0; // bit j: held candidate j is selected
+    uint32_t inbin = 0;
+#pragma unroll
+    for (int j = 0; j < N; j++) {
+        if ((valid & (1u << j)) && kk[j] >= bin_lo) {
+            if (((kk[j] - bin_lo) >> shift) >= 1u)
+                take |= 1u << j;
+            else
+                inbin |= 1u << j;
+        }
+    }
+    if (count_b <= (uint32_t)kRankList) {
+        // few members: each ranks itself against the member list
+#pragma unroll
+        for (int j = 0; j < N; j++) {
+            if (inbin & (1u << j)) {
+                const uint32_t at = atomicAdd(&ccount, 1u);
+                if (at < (uint32_t)kRankList)
+                    list[at] = u32x2{kk[j], id[j]};
+            }
+        }
+        __syncthreads();
+        const uint32_t nl = min(ccount, (uint32_t)kRankList);
+#pragma unroll
+        for (int j = 0; j < N; j++) {
+            if (inbin & (1u << j)) {
+                uint32_t rank = 0;
+#pragma unroll 8
+                for (uint32_t i = 0; i < nl; i++) {
+                    const u32x2 y = list[i];
+                    rank += (y.x > kk[j] || (y.x == kk[j] && y.y < id[j])) ? 1u : 0u;
+                }
+                if (rank < need)
+                    take |= 1u << j;
+            }
+        }
+    } else {
+        // one key shared by many members (shift == 0): lowest indices first;
+        // the held candidates are in ascending index order, thread-major, so
+        // a scan of member counts ranks them
+        uint32_t tot;
+        uint32_t rank = block_exclusive_scan<kFinThreads>((uint32_t)__popc(inbin), bs.scan, &tot);
+#pragma unroll
+        for (int j = 0; j < N; j++) {
+            if (inbin & (1u << j)) {
+                if (rank < need)
+                    take |= 1u << j;
+                rank++;
+            }
+        }
+    }
+
+    // ascending ids: one scan of the per-thread counts places every id
+    uint32_t tot;
+    uint32_t pos = block_exclusive_scan<kFinThreads>((uint32_t)__popc(take), bs.scan, &tot);
+#pragma unroll
+    for (int j = 0; j < N; j++) {
+        if ((take & (1u << j)) && pos < (uint32_t)top_k)
+            out[pos++] = (int32_t)id[j];
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // Finish: one workgroup per row. Thread t owns the contiguous run of
-// candidates [t * run, t * run + run) in registers (run <= 16), so the
+// candidates [t * run, t * run + run) in registers (run <= kFinRun), so the
 // selected ids leave in ascending order straight from registers.
 constexpr int kFinRun = kFinCap / kFinThreads; // 8
 constexpr int kFullLdsBytes = 4 * kHistBins * 4 + kCandCap * 8 + kBitmapLdsWords * 4;
@@ -645,12 +775,6 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         id[j] = e.y;
     }
 
-    // ---- exact cut: relative 12-bit digits narrow a key window to the
-    // bin holding the top_k-th candidate; the bin's members are then ranked
-    // directly under (key desc, index asc) ----
-    uint32_t *hist0 = (uint32_t *)area;                   // two histograms,
-    uint32_t *hist1 = (uint32_t *)(area + kSelBins * 4);  // then the member list
-    u32x2 *list = (u32x2 *)(area + 2 * kSelBins * 4);
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int j = 0; j < kFinRun; j++) {
@@ -660,107 +784,18 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         }
     }
     for (int i = tid; i < kSelBins; i += kFinThreads)
-        hist0[i] = 0u;
+        ((uint32_t *)area)[i] = 0u;
     if (tid == 0)
         ccount = 0u;
     block_minmax<kFinThreads>(lo, hi, &bs); // its barrier publishes the cleared bins
-    uint32_t base = lo;
-    int bits = bit_len(hi - lo); // window [base, base + 2^bits) holds every key
-    uint32_t need = (uint32_t)top_k;
-    uint32_t bin_lo = base;      // the boundary bin [bin_lo, bin_lo + 2^shift)
-    int shift = 0;
-    uint32_t count_b = (uint32_t)m;
-    uint32_t *h = hist0, *hn = hist1;
-    while (true) {
-        shift = max(bits - kSelDigit, 0);
-#pragma unroll
-        for (int j = 0; j < kFinRun; j++) {
-            if (j < n_own && kk[j] >= base) {
-                const uint32_t d = (kk[j] - base) >> shift;
-                if (d < (uint32_t)kSelBins)
-                    atomicAdd(&h[d], 1u);
-            }
-        }
+    const uint32_t valid = (1u << n_own) - 1u;
+    if (!exact_cut_write<kFinRun>(kk, id, valid, lo, hi, top_k, out, area, bs, ccount)) {
+        // the regions held fewer candidates than the counts promised
         __syncthreads();
-        for (int i = tid; i < kSelBins; i += kFinThreads)
-            hn[i] = 0u;
-        if (tid < kWave)
-            find_bin_desc_wave0(h, need, &bs);
-        __syncthreads();
-        const uint32_t b = bs.bin;
-        need -= bs.before;           // members of bin b to take
-        count_b = h[b];
-        bin_lo = base + (b << shift);
-        if (count_b <= (uint32_t)kRankList || shift == 0)
-            break;
-        base = bin_lo;
-        bits = shift;
-        uint32_t *t = h;
-        h = hn;
-        hn = t;
-        __syncthreads(); // everyone has read h[b] before it is cleared again
-    }
-    // keys >= bin_lo + 2^shift are taken, keys < bin_lo are not; the bin's
-    // members take `need` places
-    uint32_t take = 0; // bit j: owned candidate j is selected
-    uint32_t inbin = 0;
-#pragma unroll
-    for (int j = 0; j < kFinRun; j++) {
-        if (j < n_own && kk[j] >= bin_lo) {
-            if (((kk[j] - bin_lo) >> shift) >= 1u)
-                take |= 1u << j;
-            else
-                inbin |= 1u << j;
-        }
-    }
-    if (count_b <= (uint32_t)kRankList) {
-        // few members: each ranks itself against the member list
-#pragma unroll
-        for (int j = 0; j < kFinRun; j++) {
-            if (inbin & (1u << j)) {
-                const uint32_t at = atomicAdd(&ccount, 1u);
-                if (at < (uint32_t)kRankList)
-                    list[at] = u32x2{kk[j], id[j]};
-            }
-        }
-        __syncthreads();
-        const uint32_t nl = min(ccount, (uint32_t)kRankList);
-#pragma unroll
-        for (int j = 0; j < kFinRun; j++) {
-            if (inbin & (1u << j)) {
-                uint32_t rank = 0;
-#pragma unroll 8
-                for (uint32_t i = 0; i < nl; i++) {
-                    const u32x2 y = list[i];
-                    rank += (y.x > kk[j] || (y.x == kk[j] && y.y < id[j])) ? 1u : 0u;
-                }
-                if (rank < need)
-                    take |= 1u << j;
-            }
-        }
-    } else {
-        // one key shared by many members (shift == 0): lowest indices first;
-        // runs are in ascending index order, so a scan of member counts
-        // ranks them
-        uint32_t tot;
-        uint32_t rank = block_exclusive_scan<kFinThreads>((uint32_t)__popc(inbin), bs.scan, &tot);
-#pragma unroll
-        for (int j = 0; j < kFinRun; j++) {
-            if (inbin & (1u << j)) {
-                if (rank < need)
-                    take |= 1u << j;
-                rank++;
-            }
-        }
-    }
-
-    // ascending ids: one scan of the per-thread counts places every id
-    uint32_t tot;
-    uint32_t pos = block_exclusive_scan<kFinThreads>((uint32_t)__popc(take), bs.scan, &tot);
-#pragma unroll
-    for (int j = 0; j < kFinRun; j++) {
-        if ((take & (1u << j)) && pos < (uint32_t)top_k)
-            out[pos++] = (int32_t)id[j];
+        select_row_full(scores, r, L, out, cand + (int64_t)r * stride,
+                        gbitmap + (int64_t)r * (stride / 32), stride, top_k,
+                        (uint32_t(*)[kHistBins])area, (u32x2 *)(area + 4 * kHistBins * 4),
+                        (uint32_t *)(area + 4 * kHistBins * 4 + kCandCap * 8), &bs, &ccount);
     }
 }
 

@@ -1,10 +1,14 @@
 """GPU selection on crafted score rows, through the standalone dsa_topk_select
-entry point: every route of the selector (threshold from 32-token or 4-token
-group maxima, group keys held in registers or re-read, every token a
-candidate, the full-row fallback for rows whose candidates overflow) must
-give exactly the oracle's top-k under (score descending, index ascending)
-(glm5next_dsa/layer.rs source page: `select_row`, and the doc of the prefill
-row-group selector before `batch_select_enabled`)."""
+entry point: every route of the selector must give exactly the oracle's top-k
+under (score descending, index ascending) (glm5next_dsa/layer.rs source page:
+`select_row`, and the doc of the prefill row-group selector before
+`batch_select_enabled`).
+
+Three launch shapes: rows up to 131072 tokens, rows past it (more slices
+than the others), and a top_k past 2048. In each, the rows reach every route:
+the threshold from 32-token or 4-token group keys, held in registers or
+re-read; every token a candidate; the member-list and equal-key cuts; the
+full-row fallback when candidates overflow."""
 import numpy as np
 import pytest
 import torch
@@ -14,42 +18,60 @@ from sparse_attention_decode_03_amd import dsa
 
 pytestmark = pytest.mark.gpu
 
-MAX_LEN = 131072
-TOP_K = 2048
+ROUTES = {
+    "131072 tokens": (131072, 2048),
+    "135168 tokens": (135168, 2048),
+    "top_k 2304": (131072, 2304),
+}
 
 
-def crafted_rows():
+def crafted_rows(max_len, top_k):
     rng = np.random.default_rng(2024)
     rows = []
 
     def add(name, L, values):
-        full = np.zeros(MAX_LEN, np.float32)
+        L = min(L, max_len)
+        full = np.zeros(max_len, np.float32)
         full[:L] = values[:L]
         rows.append((name, L, full))
 
-    add("normal, 32-token groups", MAX_LEN, rng.standard_normal(MAX_LEN).astype(np.float32))
-    add("normal, 4-token group keys re-read", 40000,
-        rng.standard_normal(MAX_LEN).astype(np.float32))
-    add("all equal, overflow to the full-row path", 20000, np.ones(MAX_LEN, np.float32))
-    add("seven integer levels, overflow", MAX_LEN,
-        rng.integers(-3, 4, MAX_LEN).astype(np.float32))
-    add("ascending ramp", MAX_LEN, np.arange(MAX_LEN, dtype=np.float32))
-    add("descending ramp", 100000, -np.arange(MAX_LEN, dtype=np.float32))
-    add("student-t tails", MAX_LEN, rng.standard_t(3, MAX_LEN).astype(np.float32))
-    add("every token a candidate", 8191, rng.standard_normal(MAX_LEN).astype(np.float32))
-    add("one past top_k", TOP_K + 1, rng.standard_normal(MAX_LEN).astype(np.float32))
-    zeros = np.where(rng.random(MAX_LEN) < 0.5, np.float32(-0.0), np.float32(0.0))
+    n = max_len
+    add("normal, full length", n, rng.standard_normal(n).astype(np.float32))
+    add("normal, 40000 tokens", 40000, rng.standard_normal(n).astype(np.float32))
+    add("normal, 30000 tokens", 30000, rng.standard_normal(n).astype(np.float32))
+    add("all equal, overflow to the full-row path", 20000, np.ones(n, np.float32))
+    add("seven integer levels, overflow", n, rng.integers(-3, 4, n).astype(np.float32))
+    add("ascending ramp", n, np.arange(n, dtype=np.float32))
+    add("descending ramp", 100000, -np.arange(n, dtype=np.float32))
+    add("student-t tails", n, rng.standard_t(3, n).astype(np.float32))
+    add("every token a candidate", 4 * top_k - 5, rng.standard_normal(n).astype(np.float32))
+    add("exactly top_k 4-token groups", 4 * top_k - 1, rng.standard_normal(n).astype(np.float32))
+    add("one past top_k", top_k + 1, rng.standard_normal(n).astype(np.float32))
+    zeros = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0))
     zeros[rng.choice(70000, 100, replace=False)] = rng.random(100).astype(np.float32) + 0.5
     add("signed zeros with a few positives", 70000, zeros)
-    add("ties at the threshold (one decimal)", MAX_LEN,
-        np.round(rng.standard_normal(MAX_LEN), 1).astype(np.float32))
-    add("negative scores only", 50000, -np.abs(rng.standard_normal(MAX_LEN)).astype(np.float32))
+    add("ties at the threshold (one decimal)", n,
+        np.round(rng.standard_normal(n), 1).astype(np.float32))
+    add("negative scores only", 50000, -np.abs(rng.standard_normal(n)).astype(np.float32))
+    # a tight cluster (keys within ~800 units) between two far outliers: the
+    # first threshold digit is coarse, so it is narrowed over several digits
+    cluster = (1.0 + 1e-4 * rng.random(n)).astype(np.float32)
+    cluster[rng.integers(0, n)] = np.float32(1e30)
+    cluster[rng.integers(0, n)] = np.float32(-1e30)
+    add("clustered keys between far outliers", n, cluster)
+    # top-k packed into the row's last few thousand tokens
+    late = rng.standard_normal(n).astype(np.float32)
+    late[-3000:] += 50.0
+    add("winners packed at the end", n, late)
     return rows
 
 
-def test_every_selector_route_is_exact():
-    rows = crafted_rows()
+@pytest.mark.parametrize("route", list(ROUTES))
+def test_every_selector_route_is_exact(route):
+    MAX_LEN, TOP_K = ROUTES[route]
+    rows = crafted_rows(MAX_LEN, TOP_K)
     R = len(rows)
+    print(f"route {route}: max_len {MAX_LEN}, top_k {TOP_K}, {R} rows", flush=True)
     shape = dsa.Shape(num_seqs=R, rows_per_seq=1, num_heads=8, latent_dim=512, index_heads=4,
                       index_dim=64, top_k=TOP_K, page_size=64, max_len=MAX_LEN,
                       k_capacity=MAX_LEN, max_blocks_per_seq=MAX_LEN // 64, num_pages=1)
