@@ -9,8 +9,8 @@ import oracle
 from sparse_attention_decode_03_amd import dsa
 from sparse_attention_decode_03_amd import workloads as wl
 
-from gpu_common import (check_attention, check_scores, check_selection, host, run_step, small,
-                        bf16_codes_to_f64)
+from gpu_common import (ATT_ATOL, check_attention, check_scores, check_selection, host, run_step,
+                        small, bf16_codes_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,9 +160,39 @@ def test_outputs_stay_inside_their_buffers():
     check_attention(inputs, sel, out, range(R))
 
 
-def test_stage_entry_points_match_the_fused_step():
-    inputs = small(num_seqs=2, rows_per_seq=2, lengths="ragged", lo=3000, hi=7000, top_k=2048,
-                   seed=71)
+def _tied_keys_and_unmapped_pages():
+    # sequence 0: every key row equal, so every score of its rows ties and
+    # the finishing workgroup takes the full-row path; sequence 1: two pages
+    # inside its rows unmapped, so the attention skips their tokens
+    x = small(num_seqs=2, rows_per_seq=2, lengths="ragged", lo=9000, hi=10000, top_k=1024,
+              seed=72)
+    x["k_normed"][0, :] = x["k_normed"][0, 0]
+    x["block_tables"][1, 3] = -1
+    x["block_tables"][1, 10] = -1
+    return x
+
+
+STAGE_CASES = {
+    "ragged": lambda: small(num_seqs=2, rows_per_seq=2, lengths="ragged", lo=3000, hi=7000,
+                            top_k=2048, seed=71),
+    "tied keys, unmapped pages": _tied_keys_and_unmapped_pages,
+    # rows no longer than top_k: every token selected, padding resolves to -1
+    "rows within top_k": lambda: small(num_seqs=2, rows_per_seq=2, lengths="ragged", lo=100,
+                                       hi=900, top_k=1024, seed=73),
+    # 25000 pages of 4 tokens
+    "many small pages": lambda: small(num_seqs=1, rows_per_seq=1, context=100000,
+                                                    top_k=2048, page_size=4, seed=74),
+}
+
+
+@pytest.mark.parametrize("case", list(STAGE_CASES))
+def test_stage_entry_points_match_the_fused_step(case):
+    """The stage entry points, called one after another, give the fused
+    step's bytes, and both give the oracle's results: ties broken by index
+    through the full-row selection, unmapped pages skipped by the attention,
+    rows within top_k, and block tables of many small pages."""
+    inputs = STAGE_CASES[case]()
+    print(f"case {case}: lengths {inputs['seq_lens'].tolist()}", flush=True)
     fused = run_step(inputs)
     staged = dsa.DeviceStep(inputs)
     staged.index_scores()
@@ -175,6 +205,19 @@ def test_stage_entry_points_match_the_fused_step():
                                       fused.scores[r, :lens[r]].cpu().numpy())
     np.testing.assert_array_equal(staged.sel.cpu().numpy(), fused.sel.cpu().numpy())
     np.testing.assert_array_equal(staged.out.cpu().numpy(), fused.out.cpu().numpy())
+    scores, sel, out = host(fused)
+    check_selection(inputs, scores, sel, range(len(lens)))
+    # the attention skips selected tokens whose page is unmapped: the oracle
+    # (which refuses them) attends over the mapped ones
+    K, ps, bt = inputs["rows_per_seq"], inputs["page_size"], inputs["block_tables"]
+    for r in range(len(lens)):
+        ids = sel[r, :min(int(lens[r]), inputs["top_k"])]
+        keep = ids[bt[r // K, ids // ps] >= 0].astype(np.int32)
+        ref = oracle.mla_decode(inputs["q"][r:r + 1], inputs["kv_cache"], bt[r // K:r // K + 1],
+                                lens[r:r + 1], keep[None], inputs["kv_scale"], inputs["sm_scale"],
+                                1)[0]
+        err = np.abs(out[r] - ref).max()
+        assert err <= ATT_ATOL, f"row {r}: max abs error {err:.3g}"
 
 
 def test_empty_rows_and_out_of_contract_ids_are_safe():
