@@ -51,6 +51,13 @@ constexpr int kCandCap = 6144;              // full-row candidates kept in LDS (
 constexpr int kBitmapLdsWords = 12288;      // full-row bitmap in LDS up to 393216 tokens
 constexpr int kSelDigit = 12;               // bits of a threshold / cut digit
 constexpr int kSelBins = 1 << kSelDigit;    // its histogram bins
+// Those histograms sit in LDS with 16 bytes of padding after every 64 bins:
+// the wave that walks one walks 64 bins per lane, and with the padding the
+// lanes' blocks start on different banks (unpadded, every lane's 16-byte
+// read would hit the same four banks).
+constexpr int kHistPad = 4;
+constexpr int kSelHistWords = kSelBins + kSelBins / 64 * kHistPad;
+__device__ __forceinline__ uint32_t hslot(uint32_t bin) { return bin + (bin >> 6) * kHistPad; }
 constexpr int kRankList = 256;              // boundary-bin members ranked directly
 
 // Shared state of block-wide searches and reductions.
@@ -124,66 +131,48 @@ __device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
     }
 }
 
-// Descending walk over the kSelBins-bin LDS histogram h (16-byte aligned):
-// the bin where the running count first reaches `need`, the count of
-// everything above it and the histogram's total, into bs. Run by wave 0 alone (64 bins per lane, one
-// DPP lane scan); a barrier of the caller publishes the result. An
-// inconsistent histogram (total < need) yields bin 0.
+// Descending walk over the kSelBins-bin padded LDS histogram h (16-byte
+// aligned; bin b at h[hslot(b)]): the bin where the running count first
+// reaches `need`, the count of everything above it and the histogram's
+// total, into bs. Run by wave 0 alone: every lane sums its 64 bins, a lane
+// scan finds the lane whose bins cross `need`, and a second lane scan over
+// those 64 bins finds the bin. A barrier of the caller publishes the result.
+// An inconsistent histogram (total < need) yields bin 0.
 __device__ __forceinline__ void find_bin_desc_wave0(const uint32_t *h, uint32_t need,
                                                     BinSearch *bs)
 {
     constexpr int BPL = kSelBins / kWave; // 64
     const int lane = threadIdx.x;
     const int lo_b = kSelBins - BPL * (lane + 1); // lane 0 holds the top bins
-    const u32x4 *h4 = (const u32x4 *)(h + lo_b);
-    uint32_t qs[BPL / 4]; // per-quad sums of this lane's bins
+    const u32x4 *h4 = (const u32x4 *)(h + hslot(lo_b));
     uint32_t local = 0;
 #pragma unroll
     for (int q = 0; q < BPL / 4; q++) {
         const u32x4 v = h4[q];
-        qs[q] = (v.x + v.y) + (v.z + v.w);
-        local += qs[q];
+        local += (v.x + v.y) + (v.z + v.w);
     }
     const uint32_t x = wave_incl_scan_add(local);
     const uint32_t run = x - local; // count in the bins of lower lanes (higher bins)
-    if (lane == 0) {
-        bs->bin = 0u;
-        bs->before = 0u;
-    }
     if (lane == kWave - 1)
         bs->total = x;
-    if (run < need && x >= need) { // exactly one lane: its quads downwards in
-        uint32_t bef = run;        // registers, then the one quad from LDS
-        int qf = 0;
-        bool found = false;
-#pragma unroll
-        for (int q = BPL / 4 - 1; q >= 0; q--) {
-            if (!found) {
-                if (bef + qs[q] >= need) {
-                    qf = q;
-                    found = true;
-                } else {
-                    bef += qs[q];
-                }
-            }
+    const uint64_t hit = __ballot(run < need && x >= need);
+    if (hit == 0) { // inconsistent histogram
+        if (lane == 0) {
+            bs->bin = 0u;
+            bs->before = 0u;
         }
-        const u32x4 v = h4[qf];
-        const uint32_t cq[4] = {v.x, v.y, v.z, v.w};
-        uint32_t bin = (uint32_t)(lo_b + 4 * qf);
-        found = false;
-#pragma unroll
-        for (int i = 3; i >= 0; i--) {
-            if (!found) {
-                if (bef + cq[i] >= need) {
-                    bin = (uint32_t)(lo_b + 4 * qf + i);
-                    found = true;
-                } else {
-                    bef += cq[i];
-                }
-            }
-        }
-        bs->bin = bin;
-        bs->before = bef;
+        return;
+    }
+    const int lx = __ffsll((unsigned long long)hit) - 1; // the crossing lane (uniform)
+    const uint32_t run_x = (uint32_t)__builtin_amdgcn_readlane((int)run, lx);
+    // lane i: bin top - i of that lane's block, walked downwards
+    const int top = kSelBins - BPL * lx - 1;
+    const uint32_t c = h[hslot((uint32_t)(top - lane))];
+    const uint32_t y = run_x + wave_incl_scan_add(c); // count down to and with this bin
+    const uint64_t hit2 = __ballot(y >= need && y - c < need);
+    if (lane == __ffsll((unsigned long long)hit2) - 1) {
+        bs->bin = (uint32_t)(top - lane);
+        bs->before = y - c;
     }
 }
 
@@ -242,7 +231,7 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
     u32x2 *__restrict__ cand, uint32_t *__restrict__ cnt, int max_len, int stride, int top_k,
     int pmax)
 {
-    __shared__ __align__(16) uint32_t hist[kSelBins];
+    __shared__ __align__(16) uint32_t hist[kSelHistWords];
     __shared__ BinSearch bs;
     const int r = blockIdx.y;
     const int p = blockIdx.x;
@@ -307,11 +296,11 @@ __global__ __launch_bounds__(kSliceThreads) void k_select_filter(
             lo = min(lo, k);
             hi = max(hi, k);
         });
-        for (int i = tid; i < kSelBins; i += kSliceThreads)
+        for (int i = tid; i < kSelHistWords; i += kSliceThreads)
             hist[i] = 0u;
         block_minmax<kSliceThreads>(lo, hi, &bs); // its barrier also publishes the cleared bins
         const int shift = max(bit_len(hi - lo) - kSelDigit, 0);
-        for_keys([&](uint32_t k) { atomicAdd(&hist[(k - lo) >> shift], 1u); });
+        for_keys([&](uint32_t k) { atomicAdd(&hist[hslot((k - lo) >> shift)], 1u); });
         __syncthreads();
         if (tid < kWave)
             find_bin_desc_wave0(hist, (uint32_t)top_k, &bs);
@@ -557,16 +546,16 @@ __device__ __noinline__ void select_row_full(const float *__restrict__ scores, i
 }
 
 // ---------------------------------------------------------------------------
-// Exact cut and output, shared by the finishing and the whole-row
-// workgroups. The kFinThreads threads hold the row's candidates, N each,
-// thread-major in ascending token order (bit j of `valid` marks a held
-// candidate), with every candidate key in [lo, hi]. Relative 12-bit digits
-// narrow a key window to the bin holding the top_k-th candidate; the bin's
-// members are then ranked directly under (key desc, index asc), and the
-// selected ids leave in ascending order. Needs the first histogram (the
-// area's first kSelBins words) cleared and ccount zero, both published by a
-// barrier. Returns false, having written nothing, when fewer than top_k
-// candidates are held (the same answer in every thread).
+// Exact cut and output of the finishing workgroup. The kFinThreads threads
+// hold the row's candidates, N each, thread-major in ascending token order
+// (bit j of `valid` marks a held candidate), with every candidate key in
+// [lo, hi]. Relative 12-bit digits narrow a key window to the bin holding
+// the top_k-th candidate; the bin's members are then ranked directly under
+// (key desc, index asc), and the selected ids leave in ascending order.
+// Needs the first histogram (the area's first kSelHistWords words) cleared
+// and ccount zero, both published by a barrier. Returns false, having
+// written nothing, when fewer than top_k candidates are held (the same
+// answer in every thread).
 template <int N>
 __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const uint32_t (&id)[N],
                                                 uint32_t valid, uint32_t lo, uint32_t hi,
@@ -575,9 +564,9 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
 {
     static_assert(N <= 32, "one mask bit per held candidate");
     const int tid = threadIdx.x;
-    uint32_t *hist0 = (uint32_t *)area;                   // two histograms,
-    uint32_t *hist1 = (uint32_t *)(area + kSelBins * 4);  // then the member list
-    u32x2 *list = (u32x2 *)(area + 2 * kSelBins * 4);
+    uint32_t *hist0 = (uint32_t *)area;                        // two histograms,
+    uint32_t *hist1 = (uint32_t *)(area + kSelHistWords * 4);  // then the member list
+    u32x2 *list = (u32x2 *)(area + 2 * kSelHistWords * 4);
     uint32_t base = lo;
     int bits = bit_len(hi - lo); // window [base, base + 2^bits) holds every key
     uint32_t need = (uint32_t)top_k;
@@ -593,11 +582,11 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
             if ((valid & (1u << j)) && kk[j] >= base) {
                 const uint32_t d = (kk[j] - base) >> shift;
                 if (d < (uint32_t)kSelBins)
-                    atomicAdd(&h[d], 1u);
+                    atomicAdd(&h[hslot(d)], 1u);
             }
         }
         __syncthreads();
-        for (int i = tid; i < kSelBins; i += kFinThreads)
+        for (int i = tid; i < kSelHistWords; i += kFinThreads)
             hn[i] = 0u;
         if (tid < kWave)
             find_bin_desc_wave0(h, need, &bs);
@@ -607,7 +596,7 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
         first = false;
         const uint32_t b = bs.bin;
         need -= bs.before;           // members of bin b to take
-        count_b = h[b];
+        count_b = h[hslot(b)];
         bin_lo = base + (b << shift);
         if (count_b <= (uint32_t)kRankList || shift == 0)
             break;
@@ -632,13 +621,18 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
         }
     }
     if (count_b <= (uint32_t)kRankList) {
-        // few members: each ranks itself against the member list
+        // few members: each ranks itself against the member list (one
+        // atomic per thread places its members)
+        const uint32_t mine = (uint32_t)__popc(inbin);
+        uint32_t at = 0;
+        if (mine != 0u)
+            at = atomicAdd(&ccount, mine);
 #pragma unroll
         for (int j = 0; j < N; j++) {
             if (inbin & (1u << j)) {
-                const uint32_t at = atomicAdd(&ccount, 1u);
                 if (at < (uint32_t)kRankList)
                     list[at] = u32x2{kk[j], id[j]};
+                at++;
             }
         }
         __syncthreads();
@@ -689,7 +683,7 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
 // selected ids leave in ascending order straight from registers.
 constexpr int kFinRun = kFinCap / kFinThreads; // 8
 constexpr int kFullLdsBytes = 4 * kHistBins * 4 + kCandCap * 8 + kBitmapLdsWords * 4;
-static_assert(2 * kSelBins * 4 + kRankList * 8 <= kFullLdsBytes, "cut LDS must fit the area");
+static_assert(2 * kSelHistWords * 4 + kRankList * 8 <= kFullLdsBytes, "cut LDS must fit the area");
 
 __global__ __launch_bounds__(kFinThreads) void k_select_finish(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens,
@@ -783,7 +777,7 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
             hi = max(hi, kk[j]);
         }
     }
-    for (int i = tid; i < kSelBins; i += kFinThreads)
+    for (int i = tid; i < kSelHistWords; i += kFinThreads)
         ((uint32_t *)area)[i] = 0u;
     if (tid == 0)
         ccount = 0u;
