@@ -223,10 +223,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         };
 
         __syncthreads(); // rowidx, resc cleared
-        __syncthreads(); // tiles 0 and 1 staged
+        __syncthreads(); // tile 0 staged
         if (active)
             qk_softmax(0);
-        __syncthreads(); // P of step 0
+        __syncthreads(); // P of step 0, tile 1 staged
         for (int i = 0; i < nsteps; i++) {
             if (active && i + 1 < nsteps)
                 qk_softmax(i + 1);
@@ -345,21 +345,22 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     };
 
     __syncthreads(); // rowidx, resc cleared
-    // steps 0 and 1 staged, steps 2 and 3 in flight (ra holds even steps,
-    // rb odd ones; step i + 2 is staged from the buffer step i used)
+    // step 0 staged before the scoring waves start, step 1 while they score
+    // it; steps 2 and 3 in flight (ra holds even steps, rb odd ones; step
+    // i + 2 is staged from the buffer step i used)
     u32x4 ra[4], rb[4];
     gather(ra, 0);
     if (nsteps > 1)
         gather(rb, 1);
     stage(ra, 0);
+    __syncthreads(); // tile 0 staged
     if (nsteps > 2)
         gather(ra, 2);
     if (nsteps > 1)
         stage(rb, 1);
     if (nsteps > 3)
         gather(rb, 3);
-    __syncthreads(); // tiles 0 and 1 staged
-    __syncthreads(); // P of step 0
+    __syncthreads(); // P of step 0, tile 1 staged
     // step i: PV of step i and staging of step i + 2, while the scoring
     // waves score step i + 1
     for (int i = 0; i < nsteps; i++) {
