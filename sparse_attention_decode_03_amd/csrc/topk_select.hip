@@ -692,7 +692,9 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
 {
     __shared__ __align__(16) uint8_t area[kFullLdsBytes]; // full-row fallback, or the cut's
                                                           // histograms and member list
-    __shared__ uint32_t pre[kFinThreads];
+    __shared__ uint32_t pre[kFinThreads];  // candidate offset of each slice
+    __shared__ uint32_t cntl[kFinThreads]; // candidate count of each slice
+    __shared__ uint32_t cmaxl[kFinThreads / kWave]; // per-wave largest count
     __shared__ BinSearch bs;
     __shared__ uint32_t ccount;
 
@@ -712,9 +714,25 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
     const uint32_t c = tid < P ? cnt[(int64_t)r * pmax + tid] : 0u;
     uint32_t mu;
     const uint32_t off = block_exclusive_scan<kFinThreads>(c, bs.scan, &mu);
-    if (tid < P)
+    // Usually every slice's candidates fit a fixed block of tps threads,
+    // srun each (srun from the largest count), and thread t takes its share
+    // of slice t / tps directly. Otherwise they are spread evenly over the
+    // threads, each finding its slices by a search of the offsets.
+    const int tps = kFinThreads / P;
+    if (tid < P) {
         pre[tid] = off;
+        cntl[tid] = c;
+    }
+    const uint32_t cmax_w = wave_max_u32(c);
+    if (tid % kWave == 0)
+        cmaxl[tid / kWave] = cmax_w; // words of their own: read after the barrier, never rewritten
     __syncthreads();
+    uint32_t cmax = 0;
+#pragma unroll
+    for (int w = 0; w < kFinThreads / kWave; w++)
+        cmax = max(cmax, cmaxl[w]);
+    const int srun = ((int)cmax + tps - 1) / tps;
+    const bool by_slice = srun <= kFinRun;
     const int m = (int)mu;
 
     if (m < top_k || m > kFinCap) {
@@ -727,46 +745,63 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
         return;
     }
 
-    // this thread's run, gathered from the slices' regions (all loads in
-    // flight at once; indices past the run repeat the last candidate)
-    const int run = (m + kFinThreads - 1) / kFinThreads;
-    const int i0 = min(tid * run, m);
-    const int n_own = min(run, m - i0);
-    int sl = 0; // slice of candidate min(i0, m - 1): last offset <= it
-    {
-        const int i = min(i0, m - 1);
-        int lo = 0, hi = P - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= (uint32_t)i)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        sl = lo;
-    }
-    // the run usually stays inside one slice: keep that slice's bounds in
-    // registers and touch LDS again only when the run crosses into the next
-    int src_off[kFinRun];
-    int sl_lo = (int)pre[sl];
-    int sl_hi = sl + 1 < P ? (int)pre[sl + 1] : m; // first candidate of the next slice
-#pragma unroll
-    for (int j = 0; j < kFinRun; j++) {
-        const int i = min(i0 + min(j, max(n_own - 1, 0)), m - 1);
-        while (i >= sl_hi) {
-            sl++;
-            sl_lo = sl_hi;
-            sl_hi = sl + 1 < P ? (int)pre[sl + 1] : m;
-        }
-        src_off[j] = sl * kSelSlice + (i - sl_lo);
-    }
     const u32x2 *src = cand + (int64_t)r * stride;
     uint32_t kk[kFinRun], id[kFinRun];
+    int n_own;
+    if (by_slice) {
+        const int p = tid / tps; // threads past P * tps hold nothing
+        const int u = tid % tps;
+        const int cp = p < P ? (int)cntl[p] : 0;
+        n_own = min(srun, max(cp - u * srun, 0));
+        const u32x2 *sp = src + (int64_t)min(p, P - 1) * kSelSlice + u * srun;
 #pragma unroll
-    for (int j = 0; j < kFinRun; j++) {
-        const u32x2 e = src[src_off[j]];
-        kk[j] = e.x;
-        id[j] = e.y;
+        for (int j = 0; j < kFinRun; j++) {
+            u32x2 e = u32x2{0u, 0u};
+            if (j < n_own)
+                e = sp[j];
+            kk[j] = e.x;
+            id[j] = e.y;
+        }
+    } else {
+        // this thread's run, gathered from the slices' regions (all loads in
+        // flight at once; indices past the run repeat the last candidate)
+        const int run = (m + kFinThreads - 1) / kFinThreads;
+        const int i0 = min(tid * run, m);
+        n_own = min(run, m - i0);
+        int sl = 0; // slice of candidate min(i0, m - 1): last offset <= it
+        {
+            const int i = min(i0, m - 1);
+            int lo = 0, hi = P - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (pre[mid] <= (uint32_t)i)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            sl = lo;
+        }
+        // the run usually stays inside one slice: keep that slice's bounds in
+        // registers and touch LDS again only when the run crosses into the next
+        int src_off[kFinRun];
+        int sl_lo = (int)pre[sl];
+        int sl_hi = sl + 1 < P ? (int)pre[sl + 1] : m; // first candidate of the next slice
+#pragma unroll
+        for (int j = 0; j < kFinRun; j++) {
+            const int i = min(i0 + min(j, max(n_own - 1, 0)), m - 1);
+            while (i >= sl_hi) {
+                sl++;
+                sl_lo = sl_hi;
+                sl_hi = sl + 1 < P ? (int)pre[sl + 1] : m;
+            }
+            src_off[j] = sl * kSelSlice + (i - sl_lo);
+        }
+#pragma unroll
+        for (int j = 0; j < kFinRun; j++) {
+            const u32x2 e = src[src_off[j]];
+            kk[j] = e.x;
+            id[j] = e.y;
+        }
     }
 
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
