@@ -13,6 +13,10 @@
 //    loads (the next tile's loads are in flight while the current tile
 //    computes) and are parked in LDS with an XOR swizzle, then re-read in
 //    matrix-core operand order without bank conflicts.
+//  - The keys are read once, so their loads carry the non-temporal hint:
+//    the stream then no longer evicts the scores this pass writes from L2,
+//    whose dirty lines would otherwise reach HBM a few at a time in the
+//    middle of the read stream (measured: 12 % of the pass).
 //  - The contraction is a 32x32x16 bf16 MFMA with the (up to 32) index heads
 //    as M and 32 tokens as N; D is the reduction. A lane ends with 16 head
 //    partials of one token; ReLU, weight and head sum run in fp32 in a fixed
@@ -21,6 +25,8 @@
 //    of each aligned 4-token and 32-token group (cross-lane max of the
 //    finished scores, two stores per 32 tokens). Selection draws its
 //    threshold from these.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -111,17 +117,34 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 
     const uint16_t *kseq = k_normed + (int64_t)s * cap * D;
     u32x4 regs[LOADS];
-    auto load_tile = [&](int tile) {
+    // loads [I0, I1) of a tile's share of this thread
+    auto load_part = [&](int tile, auto i0c, auto i1c) {
+        constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
         const int t0 = tile * kIdxTile;
 #pragma unroll
-        for (int i = 0; i < LOADS; i++) {
+        for (int i = I0; i < I1; i++) {
             const int g = i * kIdxThreads + tid;
             const int row = g / CH;
             const int c = g % CH;
             if (t0 + row < lmax)
-                regs[i] = *(const u32x4 *)(kseq + (int64_t)(t0 + row) * D + c * 8);
+                regs[i] = __builtin_nontemporal_load(
+                    (const u32x4 *)(kseq + (int64_t)(t0 + row) * D + c * 8));
             else
                 regs[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    using IC0 = std::integral_constant<int, 0>;
+    using ICH = std::integral_constant<int, LOADS / 2>;
+    using ICL = std::integral_constant<int, LOADS>;
+    // a tile's registers into LDS (XOR swizzle), half [I0, I1)
+    auto park_part = [&](auto i0c, auto i1c) {
+        constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+#pragma unroll
+        for (int i = I0; i < I1; i++) {
+            const int g = i * kIdxThreads + tid;
+            const int row = g / CH;
+            const int c = g % CH;
+            lds[row * CH + (c ^ (row & (CH - 1)))] = regs[i];
         }
     };
 
@@ -196,20 +219,21 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         load_row(s * K + loaded);
     }
 
-    load_tile(tile_first);
+    load_part(tile_first, IC0{}, ICL{});
     for (int tile = tile_first; tile < tile_end; tile += W) {
         const int t0 = tile * kIdxTile;
+        const bool more = tile + W < tile_end;
         __syncthreads(); // every wave is done reading the previous tile
-#pragma unroll
-        for (int i = 0; i < LOADS; i++) {
-            const int g = i * kIdxThreads + tid;
-            const int row = g / CH;
-            const int c = g % CH;
-            lds[row * CH + (c ^ (row & (CH - 1)))] = regs[i];
-        }
+        // park the tile in LDS half by half; each half's registers take the
+        // next tile's loads at once, so the loads stay in flight while this
+        // tile is parked and computed
+        park_part(IC0{}, ICH{});
+        if (more)
+            load_part(tile + W, IC0{}, ICH{});
+        park_part(ICH{}, ICL{});
+        if (more)
+            load_part(tile + W, ICH{}, ICL{});
         __syncthreads();
-        if (tile + W < tile_end)
-            load_tile(tile + W); // in flight while this tile computes
 
         if (ONE_ROW) {
             // key operands: column (token) lane%32, k-chunks hl*KS + ks
