@@ -62,6 +62,10 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
+// G: heads per workgroup (64 or 32). Each head's arithmetic is the same
+// whichever heads share its workgroup (a head whose reference did not move
+// rescales by exactly 1), so G changes where the work runs, never a result.
+template <int G>
 __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
     const int32_t *__restrict__ bt, const int32_t *__restrict__ seq_lens,
@@ -70,12 +74,14 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
     __shared__ u32x4 tile[kTiles][kStep * kRowStride];   // bf16 tokens x latent, padded rows
-    __shared__ __align__(16) uint8_t pbuf[2][kAttHeads * kPRowBytes]; // bf16 P, PV k order
-    __shared__ __align__(16) float alds[2][kAttHeads];   // per-head rescale factors
-    __shared__ float2 mlds[kAttHeads];                   // per-head (m, l) at the end
+    __shared__ __align__(16) uint8_t pbuf[2][G * kPRowBytes]; // bf16 P, PV k order
+    __shared__ __align__(16) float alds[2][G];   // per-head rescale factors
+    __shared__ float2 mlds[G];                   // per-head (m, l) at the end
     __shared__ int rowidx[kAttChunk];                    // latent row of each slot, -1 = skip
     __shared__ int resc[kMaxSteps];                      // step s: O needs its alphas
 
+    constexpr int kHt = G / 16; // 16-head MFMA tiles of the group
+    static_assert(kHt >= 1 && kHt <= 4, "one scoring wave per 16 heads");
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
@@ -88,13 +94,13 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int L = min(max(seq_lens[r], 0), max_len);
     const int n = min(top_k, L);
     const int nch = (n + kAttChunk - 1) / kAttChunk;
-    const int h0 = hg * kAttHeads;         // first head of the group
-    const int nh = min(kAttHeads, H - h0); // heads of the group that exist
+    const int h0 = hg * G;         // first head of the group
+    const int nh = min(G, H - h0); // heads of the group that exist
     const int mt_count = (nh + 15) / 16;   // 16-head tiles that exist
 
     if (n == 0) {
         if (c == 0) {
-            for (int i = tid; i < kAttHeads * kLat; i += kAttThreads) {
+            for (int i = tid; i < G * kLat; i += kAttThreads) {
                 const int h = h0 + i / kLat;
                 if (h < H)
                     out[((int64_t)r * H + h) * kLat + (i % kLat)] = 0;
@@ -124,17 +130,17 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     if (tid < kMaxSteps)
         resc[tid] = 0;
     // P rows of heads that no scoring wave covers stay zero
-    for (int i = tid; i < 2 * kAttHeads * kPRowBytes / 16; i += kAttThreads)
+    for (int i = tid; i < 2 * G * kPRowBytes / 16; i += kAttThreads)
         ((u32x4 *)pbuf)[i] = u32x4{0u, 0u, 0u, 0u};
 
     if (wave < 4) {
         // ================= scoring waves: QK + online softmax =================
         const int hl = wave * 16 + n16; // this lane's head within the group
-        const bool active = wave * 16 < nh;
+        const bool active = wave < kHt && wave * 16 < nh;
         // query of head hl, latent dims 32 ks + 8 g .. +7 (the B operand);
         // branch-free, a missing head loads head H-1 and is zeroed
         u32x4 qr[16];
-        {
+        if (active) {
             const uint16_t *qrow = q + ((int64_t)r * H + min(h0 + hl, H - 1)) * kLat + 8 * g;
 #pragma unroll
             for (int ks = 0; ks < 16; ks++) {
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         if (active && g == 0) {
             mlds[hl] = float2{m_run, l_all};
             if (nch > 1) {
-                const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
+                const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * G;
                 part_ml[pbase + hl] = float2{m_run, l_all};
             }
         }
@@ -251,9 +257,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int ptid = tid - 4 * kWave; // 0..255
     const int tq = ptid >> 5;         // staging: tokens 4 tq .. 4 tq + 3
     const int dc = ptid & 31;         //          latent bytes 16 dc .. 16 dc + 15
-    floatx4 o[4][kPvTiles]; // O[head 16 mt + n16][columns kPvCols v + 16 nt + 4 g + e]
+    floatx4 o[kHt][kPvTiles]; // O[head 16 mt + n16][columns kPvCols v + 16 nt + 4 g + e]
 #pragma unroll
-    for (int mt = 0; mt < 4; mt++)
+    for (int mt = 0; mt < kHt; mt++)
 #pragma unroll
         for (int nt = 0; nt < kPvTiles; nt++)
             o[mt][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         const char *p1 = p0 + 16 * (kRowStride * 16);
         if (rs) {
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++) {
+            for (int mt = 0; mt < kHt; mt++) {
                 const float a = alds[step & 1][16 * mt + n16];
 #pragma unroll
                 for (int nt = 0; nt < kPvTiles; nt++) {
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         // every operand of the step is requested before the first product
         bf16x8 pa[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
+        for (int mt = 0; mt < kHt; mt++)
             pa[mt] = as_bf16x8(*(const u32x4 *)(pb + (16 * mt + n16) * kPRowBytes + 16 * g));
         shortx8 vb[kPvTiles];
 #pragma unroll
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 #pragma unroll
         for (int nt = 0; nt < kPvTiles; nt++) {
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++) // head tiles past the group's heads see P = 0
+            for (int mt = 0; mt < kHt; mt++) // head tiles past the group's heads see P = 0
                 o[mt][nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vb[nt]), pa[mt], o[mt][nt]);
         }
     };
@@ -385,12 +391,12 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     // back as whole 256-byte head rows with 16-byte stores. Only this wave
     // touches its region, so a wait for its own LDS writes is enough.
     constexpr int kORowBytes = 2 * kPvCols + 16; // padded: 16 rows at one column spread over the banks
-    static_assert(4 * kAttHeads * kORowBytes <= (int)sizeof(tile), "O blocks fit the tiles");
-    uint8_t *oreg = (uint8_t *)tile + v * (kAttHeads * kORowBytes);
-    const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * kAttHeads;
+    static_assert(4 * G * kORowBytes <= (int)sizeof(tile), "O blocks fit the tiles");
+    uint8_t *oreg = (uint8_t *)tile + v * (G * kORowBytes);
+    const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * G;
     auto park = [&](auto scale_of) {
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
+        for (int mt = 0; mt < kHt; mt++) {
             const int hl = 16 * mt + n16;
             const float sc = scale_of(hl);
 #pragma unroll
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     // lane: 16 bytes (8 columns) of head row 4 i + (lane >> 4)
     const int cb = 16 * (lane & 15);
 #pragma unroll
-    for (int i = 0; i < kAttHeads / 4; i++) {
+    for (int i = 0; i < G / 4; i++) {
         const int hl = 4 * i + (lane >> 4);
         const int h = h0 + hl;
         const u32x4 val = *(const u32x4 *)(oreg + hl * kORowBytes + cb);
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ 
                                                    const int32_t *__restrict__ seq_lens,
                                                    uint16_t *__restrict__ out, int H, int top_k,
                                                    int max_len, int nch_max, int hg_count,
-                                                   float kv_scale)
+                                                   int G, float kv_scale)
 {
     const int r = blockIdx.y;
     const int h = blockIdx.x;
@@ -443,8 +449,8 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ 
     const int nch = (n + kAttChunk - 1) / kAttChunk;
     if (nch <= 1)
         return;
-    const int hg = h / kAttHeads;
-    const int hl = h % kAttHeads;
+    const int hg = h / G;
+    const int hl = h % G;
     const int d = threadIdx.x * 4;
     float m_acc = kNegInf, l_acc = 0.0f;
     floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ 
         for (int k = 0; k < kB; k++) {
             // branch-free: chunks past the row's last re-read its last one
             const int64_t pi =
-                (((int64_t)r * hg_count + hg) * nch_max + min(c0 + k, nch - 1)) * kAttHeads + hl;
+                (((int64_t)r * hg_count + hg) * nch_max + min(c0 + k, nch - 1)) * G + hl;
             ml[k] = part_ml[pi];
             const u32x2 pk = *(const u32x2 *)(part_o + pi * kLat + d);
             ov[k] = floatx4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
@@ -488,26 +494,59 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ 
     *(u32x2 *)orow = packed;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
                       float kv_scale, float sm_scale, uint16_t *out, char *ws,
                       const Workspace &wl, hipStream_t stream)
 {
     const int nch_max = att_chunks(ls) > 0 ? att_chunks(ls) : 1;
-    const int hgc = att_head_groups(ls);
     const float qk_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634074);
     uint16_t *part_o = (uint16_t *)(ws + wl.part_o);
     float2 *part_ml = (float2 *)(ws + wl.part_ml);
-    hipLaunchKernelGGL(k_mla_decode, dim3(nch_max * hgc, ls.num_rows), dim3(kAttThreads), 0,
-                       stream, q, kv_cache, block_tables, seq_lens, sel, part_o, part_ml, out,
-                       ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size, ls.max_blocks,
-                       ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max, hgc);
+    // Heads per workgroup: 32 while that still leaves at most one workgroup
+    // per CU (a small batch: twice the workgroups, each pulling half the
+    // query through its CU), else 64 (a large batch: the latent rows are
+    // gathered once per 64 heads). Results do not depend on the choice. The
+    // partials of either fit the workspace, which is sized for groups of 64.
+    const int hg32 = (ls.num_heads + 31) / 32;
+    const bool small = (int64_t)ls.num_rows * nch_max * hg32 <= device_cus();
+    const int G = small ? 32 : kAttHeads;
+    const int hgc = (ls.num_heads + G - 1) / G;
+    if (small)
+        hipLaunchKernelGGL(k_mla_decode<32>, dim3(nch_max * hgc, ls.num_rows), dim3(kAttThreads),
+                           0, stream, q, kv_cache, block_tables, seq_lens, sel, part_o, part_ml,
+                           out, ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size,
+                           ls.max_blocks, ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max,
+                           hgc);
+    else
+        hipLaunchKernelGGL(k_mla_decode<kAttHeads>, dim3(nch_max * hgc, ls.num_rows),
+                           dim3(kAttThreads), 0, stream, q, kv_cache, block_tables, seq_lens, sel,
+                           part_o, part_ml, out, ls.rows_per_seq, ls.num_heads, ls.top_k,
+                           ls.page_size, ls.max_blocks, ls.num_pages, ls.max_len, kv_scale,
+                           qk_log2, nch_max, hgc);
     if (hipGetLastError() != hipSuccess)
         return -1;
     if (nch_max > 1) {
         hipLaunchKernelGGL(k_mla_merge, dim3(ls.num_heads, ls.num_rows), dim3(128), 0, stream,
                            part_o, part_ml, seq_lens, out, ls.num_heads, ls.top_k, ls.max_len,
-                           nch_max, hgc, kv_scale);
+                           nch_max, hgc, G, kv_scale);
         if (hipGetLastError() != hipSuccess)
             return -1;
     }
