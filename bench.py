@@ -69,13 +69,16 @@ def load_traffic():
 
 
 def cpu_baseline(inputs: dict, budget_s: float = 12.0) -> dict:
+    """The oracle on the host cores: rows of the workload evaluated one after
+    another (cycling over them) until about `budget_s` of CPU work, scaled to
+    steps of the workload's row count."""
     import oracle
     K = inputs["rows_per_seq"]
     R = inputs["seq_lens"].shape[0]
     t0 = time.perf_counter()
     done = 0
-    for r in range(R):
-        oracle.decode(inputs, rows=[r])
+    while True:
+        oracle.decode(inputs, rows=[done % R])
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -83,8 +86,9 @@ def cpu_baseline(inputs: dict, budget_s: float = 12.0) -> dict:
     rows_per_s = done / dt
     return {"value": rows_per_s / R, "unit": "steps/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{done} of {R} rows (each row: fp64 scores over its whole context, full-sort "
-                      f"top-k, two-pass softmax attention), {dt:.1f} s, scaled to steps of {R} rows",
+            "sample": f"{done} row evaluations cycling over the workload's {R} rows (each: fp64 "
+                      f"scores over the row's whole context, full-sort top-k, two-pass softmax "
+                      f"attention), {dt:.1f} s, scaled to steps of {R} rows",
             "rows_per_seq": K}
 
 

@@ -9,7 +9,8 @@
 // Decomposition (a function of the row alone, never of R, so every row is
 // bit-reproducible whichever rows share a launch):
 //  - A row's selection is cut into chunks of kAttChunk slots. One workgroup
-//    of 8 waves covers one chunk for 64 heads, in steps of 32 tokens. Each
+//    of 8 waves covers one chunk for a group of G heads (16, 32 or 64), in
+//    steps of 32 tokens. Each
 //    token's 512-byte FP8 row is gathered through the block table with
 //    coalesced 16-byte loads, dequantised exactly to bf16 (E4M3 is a subset
 //    of bf16; kv_scale is folded into the logit scale and the output) and
@@ -20,7 +21,7 @@
 //    on 16x16x32 bf16 MFMA (the tile as A, the query as B), then the online
 //    softmax in fp32 (log2 domain, exp2, fixed-order reductions, lazy
 //    rescale); the bf16 probabilities go to a small LDS buffer in the PV
-//    operand's k order. Waves 4-7 accumulate: wave v holds O[64 heads,
+//    operand's k order. Waves 4-7 accumulate: wave v holds O[G heads,
 //    latent columns 128v..128v+127] and runs PV on 16x16x32 bf16 MFMA (P as
 //    A, the tile as B through LDS transpose loads, ds_read_tr16_b64); they
 //    also dequantise and stage the tiles and keep the gathers in flight.
@@ -57,14 +58,17 @@ constexpr int kRowStride = kRowChunks + 2; // in 16-byte chunks
 constexpr int kPRowBytes = 80;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kGatherDepth = 4;   // gather lookahead in steps, 16- and 32-head groups
+constexpr int kGatherDepth64 = 2; // and 64-head groups
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-// G: heads per workgroup (64 or 32). Each head's arithmetic is the same
-// whichever heads share its workgroup (a head whose reference did not move
-// rescales by exactly 1), so G changes where the work runs, never a result.
+// G: heads per workgroup (16, 32 or 64; scoring waves past G / 16 idle).
+// Each head's arithmetic is the same whichever heads share its workgroup (a
+// head whose reference did not move rescales by exactly 1), so G changes
+// where the work runs, never a result.
 template <int G>
 __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
@@ -81,6 +85,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     __shared__ int resc[kMaxSteps];                      // step s: O needs its alphas
 
     constexpr int kHt = G / 16; // 16-head MFMA tiles of the group
+    // steps of gathers in flight: as deep as the accumulators leave registers
+    // for (each step is 16 VGPRs per accumulating lane; 64 heads keep 128 in O)
+    constexpr int kDepth = G == 64 ? kGatherDepth64 : kGatherDepth;
     static_assert(kHt >= 1 && kHt <= 4, "one scoring wave per 16 heads");
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -351,42 +358,69 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     };
 
     __syncthreads(); // rowidx, resc cleared
-    // step 0 staged before the scoring waves start, step 1 while they score
-    // it; steps 2 and 3 in flight (ra holds even steps, rb odd ones; step
-    // i + 2 is staged from the buffer step i used)
-    u32x4 ra[4], rb[4];
-    gather(ra, 0);
-    if (nsteps > 1)
-        gather(rb, 1);
-    stage(ra, 0);
+    // Gathers run kDepth steps ahead: buffer j % kDepth holds step j's rows
+    // from the step that issues its loads until the step that stages it.
+    // Step 0 is staged before the scoring waves start and step 1 while they
+    // score it; step i + 2 is staged during step i, and its buffer then
+    // takes the loads of step i + 2 + kDepth.
+    // Prologue gathers are issued whatever the chunk's step count (a step
+    // past the chunk reads latent row 0 and is never staged). With 16- and
+    // 32-head groups the step loop is unrolled (at most kMaxSteps steps), so
+    // every buffer index is a constant and the loads outstanding at each
+    // stage are the same on every path: the compiler's wait before a stage
+    // then covers exactly that step's loads, not the later steps' still in
+    // flight (measured: attention at 8 x 131072 from 14.4 to 12.4 us).
+    u32x4 rbuf[kDepth][4];
+#pragma unroll
+    for (int j = 0; j < kDepth; j++)
+        gather(rbuf[j], j);
+    __builtin_amdgcn_sched_barrier(0); // every prologue load issued before the first wait
+    stage(rbuf[0], 0);
     __syncthreads(); // tile 0 staged
-    if (nsteps > 2)
-        gather(ra, 2);
+    gather(rbuf[0], kDepth);
     if (nsteps > 1)
-        stage(rb, 1);
-    if (nsteps > 3)
-        gather(rb, 3);
+        stage(rbuf[1], 1);
+    gather(rbuf[1 % kDepth], kDepth + 1);
     __syncthreads(); // P of step 0, tile 1 staged
     // step i: PV of step i and staging of step i + 2, while the scoring
     // waves score step i + 1
-    for (int i = 0; i < nsteps; i++) {
-        if (i + 2 < nsteps) {
-            if ((i & 1) == 0) {
-                stage(ra, i + 2);
-                if (i + 4 < nsteps)
-                    gather(ra, i + 4);
-            } else {
-                stage(rb, i + 2);
-                if (i + 4 < nsteps)
-                    gather(rb, i + 4);
+    if constexpr (G == 64) {
+        // A rolled loop (unrolled, the 64-head accumulators and the rows in
+        // flight need more registers than a wave has): the buffer of a step
+        // is picked at run time, and a gather is issued only for a step the
+        // chunk has.
+        for (int i = 0; i < nsteps; i++) {
+            if (i + 2 < nsteps) {
+#pragma unroll
+                for (int b = 0; b < kDepth; b++) {
+                    if (b == (i + 2) % kDepth) {
+                        stage(rbuf[b], i + 2);
+                        if (i + 2 + kDepth < nsteps)
+                            gather(rbuf[b], i + 2 + kDepth);
+                    }
+                }
             }
+            pv(i);
+            __syncthreads();
         }
-        pv(i);
-        __syncthreads();
+    } else {
+#pragma unroll
+        for (int i = 0; i < kMaxSteps; i++) {
+            if (i >= nsteps)
+                break;
+            if (i + 2 < nsteps)
+                stage(rbuf[(i + 2) % kDepth], i + 2);
+            // steps past kMaxSteps are dropped at compile time; one past the
+            // chunk's last step is a wasted read of latent row 0
+            if (i + 2 + kDepth < kMaxSteps)
+                gather(rbuf[(i + 2) % kDepth], i + 2 + kDepth);
+            pv(i);
+            __syncthreads();
+        }
     }
     __syncthreads(); // mlds
 
-    // Output through LDS: each wave parks its O block (64 heads x its 128
+    // Output through LDS: each wave parks its O block (G heads x its 128
     // columns, bf16) in its own region of the now idle tiles, then writes it
     // back as whole 256-byte head rows with 16-byte stores. Only this wave
     // touches its region, so a wait for its own LDS writes is enough.
@@ -520,27 +554,24 @@ int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *k
     const float qk_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634074);
     uint16_t *part_o = (uint16_t *)(ws + wl.part_o);
     float2 *part_ml = (float2 *)(ws + wl.part_ml);
-    // Heads per workgroup: 32 while that still leaves at most one workgroup
-    // per CU (a small batch: twice the workgroups, each pulling half the
-    // query through its CU), else 64 (a large batch: the latent rows are
-    // gathered once per 64 heads). Results do not depend on the choice. The
-    // partials of either fit the workspace, which is sized for groups of 64.
-    const int hg32 = (ls.num_heads + 31) / 32;
-    const bool small = (int64_t)ls.num_rows * nch_max * hg32 <= device_cus();
-    const int G = small ? 32 : kAttHeads;
+    // Heads per workgroup: the smallest of 16, 32 and 64 that still leaves at
+    // most one workgroup per CU (a small batch spreads over more CUs, each
+    // pulling a part of the query; a large batch gathers the latent rows
+    // once per 64 heads). Results do not depend on the choice. The partials
+    // of any of them fit the workspace, which is sized for groups of 64.
+    const int64_t units = (int64_t)ls.num_rows * nch_max;
+    int G = kAttHeads;
+    if (units * ((ls.num_heads + 15) / 16) <= device_cus())
+        G = 16;
+    else if (units * ((ls.num_heads + 31) / 32) <= device_cus())
+        G = 32;
     const int hgc = (ls.num_heads + G - 1) / G;
-    if (small)
-        hipLaunchKernelGGL(k_mla_decode<32>, dim3(nch_max * hgc, ls.num_rows), dim3(kAttThreads),
-                           0, stream, q, kv_cache, block_tables, seq_lens, sel, part_o, part_ml,
-                           out, ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size,
-                           ls.max_blocks, ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max,
-                           hgc);
-    else
-        hipLaunchKernelGGL(k_mla_decode<kAttHeads>, dim3(nch_max * hgc, ls.num_rows),
-                           dim3(kAttThreads), 0, stream, q, kv_cache, block_tables, seq_lens, sel,
-                           part_o, part_ml, out, ls.rows_per_seq, ls.num_heads, ls.top_k,
-                           ls.page_size, ls.max_blocks, ls.num_pages, ls.max_len, kv_scale,
-                           qk_log2, nch_max, hgc);
+    const dim3 grid(nch_max * hgc, ls.num_rows);
+    auto kern = G == 16 ? k_mla_decode<16> : G == 32 ? k_mla_decode<32> : k_mla_decode<kAttHeads>;
+    hipLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, q, kv_cache, block_tables,
+                       seq_lens, sel, part_o, part_ml, out, ls.rows_per_seq, ls.num_heads,
+                       ls.top_k, ls.page_size, ls.max_blocks, ls.num_pages, ls.max_len, kv_scale,
+                       qk_log2, nch_max, hgc);
     if (hipGetLastError() != hipSuccess)
         return -1;
     if (nch_max > 1) {
