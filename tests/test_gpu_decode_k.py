@@ -48,10 +48,10 @@ def assert_serial_equals_batched(inputs):
 
 @pytest.mark.parametrize("K,seed", [(2, 1), (4, 2), (8, 3)])
 def test_verify_rows_bit_identical_to_serial_calls(K, seed):
-    # With K >= 4 the K-row call has enough (row, chunk) work to run the
-    # attention in 64-head workgroups while each serial call runs 32-head
-    # ones: the bytes must still agree (a head's arithmetic never depends on
-    # the heads that share its workgroup).
+    # The K-row call has more (row, chunk) work than each serial call, so
+    # the attention runs in larger head groups: 16 heads for the serial
+    # calls, 16, 32 and 64 for K = 2, 4 and 8. The bytes must still agree (a
+    # head's arithmetic never depends on the heads that share its workgroup).
     inputs = small(num_seqs=3, rows_per_seq=K, lengths="verify", base=4500, top_k=2048,
                    seed=100 + seed)
     assert_serial_equals_batched(inputs)
