@@ -174,13 +174,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     if (ONE_ROW)
         load_row(s);
 
-    // One 32-token block of row r: MFMA over D, ReLU-weighted head sum, the
-    // score store and (GM) the group maxima of the block.
-    auto score_block = [&](int r, int L, int t0, int col0, const bf16x8 (&kb)[KS]) {
-        floatx16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            acc = mfma32x32x16(qa[ks], kb[ks], acc);
+    // The epilogue of one 32-token block of row r from its MFMA result:
+    // ReLU-weighted head sum, the score store and (GM) the group maxima.
+    auto block_out = [&](int r, int L, int t0, int col0, const floatx16 &acc) {
         float part = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; v++)
@@ -204,6 +200,33 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
             if (lane == 0 && t < L)
                 gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k32;
         }
+    };
+    // One 32-token block: MFMA over D, then the epilogue.
+    auto score_block = [&](int r, int L, int t0, int col0, const bf16x8 (&kb)[KS]) {
+        floatx16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            acc = mfma32x32x16(qa[ks], kb[ks], acc);
+        block_out(r, L, t0, col0, acc);
+    };
+    // Two neighbouring blocks of one row: their MFMA chains interleaved, so
+    // each product's latency hides behind the other chain (the arithmetic of
+    // every element is that of score_block).
+    // The key operands are read from LDS inside the k loop (the registers
+    // also hold the next tile's loads).
+    auto score_block_pair = [&](int r, int L, int t0, int col0) {
+        floatx16 acc[2] = {};
+        const int row0 = col0 + (lane & 31), row1 = row0 + 32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const int c = hl * KS + ks;
+            const bf16x8 k0 = as_bf16x8(lds[row0 * CH + (c ^ (row0 & (CH - 1)))]);
+            const bf16x8 k1 = as_bf16x8(lds[row1 * CH + (c ^ (row1 & (CH - 1)))]);
+            acc[0] = mfma32x32x16(qa[ks], k0, acc[0]);
+            acc[1] = mfma32x32x16(qa[ks], k1, acc[1]);
+        }
+        block_out(r, L, t0, col0, acc[0]);
+        block_out(r, L, t0, col0 + 32, acc[1]);
     };
 
     // Several rows (K > 1): the tile's K x 8 (row, block) items are split
@@ -252,9 +275,12 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
             for (int b = 0; b < 2; b++)
                 score_block(s, L, t0, wave * 64 + b * 32, kb[b]);
         } else {
-            // the wave's (row, 32-token block) items, rows of one item range
-            // reuse the loaded query
-            for (int it = item0; it < item0 + items; it++) {
+            // the wave's (row, 32-token block) items, two at a time: a range
+            // starts at an even item and the blocks per row are even, so a
+            // pair never straddles rows. Rows of one item range reuse the
+            // loaded query. A pair runs when its first block is inside the
+            // row (the second one's stores are masked past L).
+            for (int it = item0; it < item0 + items; it += 2) {
                 const int j = it / kBlocks;
                 const int blk = it % kBlocks;
                 const int r = s * K + j;
@@ -265,14 +291,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                     load_row(r);
                     loaded = j;
                 }
-                bf16x8 kb[KS];
-                const int row = blk * 32 + (lane & 31);
-#pragma unroll
-                for (int ks = 0; ks < KS; ks++) {
-                    const int c = hl * KS + ks;
-                    kb[ks] = as_bf16x8(lds[row * CH + (c ^ (row & (CH - 1)))]);
-                }
-                score_block(r, L, t0, blk * 32, kb);
+                score_block_pair(r, L, t0, blk * 32);
             }
         }
     }
