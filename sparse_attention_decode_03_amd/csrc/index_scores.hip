@@ -217,13 +217,25 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     auto score_block_pair = [&](int r, int L, int t0, int col0) {
         floatx16 acc[2] = {};
         const int row0 = col0 + (lane & 31), row1 = row0 + 32;
+        auto key = [&](int row, int ks) {
+            const int c = hl * KS + ks;
+            return as_bf16x8(lds[row * CH + (c ^ (row & (CH - 1)))]);
+        };
+        // operands of step ks + 1 requested before the products of step ks
+        bf16x8 k0 = key(row0, 0), k1 = key(row1, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
-            const int c = hl * KS + ks;
-            const bf16x8 k0 = as_bf16x8(lds[row0 * CH + (c ^ (row0 & (CH - 1)))]);
-            const bf16x8 k1 = as_bf16x8(lds[row1 * CH + (c ^ (row1 & (CH - 1)))]);
+            bf16x8 n0 = k0, n1 = k1;
+            if (ks + 1 < KS) {
+                n0 = key(row0, ks + 1);
+                n1 = key(row1, ks + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             acc[0] = mfma32x32x16(qa[ks], k0, acc[0]);
             acc[1] = mfma32x32x16(qa[ks], k1, acc[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            k0 = n0;
+            k1 = n1;
         }
         block_out(r, L, t0, col0, acc[0]);
         block_out(r, L, t0, col0 + 32, acc[1]);
