@@ -120,6 +120,30 @@ __device__ __forceinline__ uint32_t wave_incl_scan_add(uint32_t x)
     const int row = (threadIdx.x & 63) >> 4;
     return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
+// Pairwise combination of lanes l and l ^ 32 (and of l and l ^ 16 within
+// each 32-lane half) through the gfx950 lane-swap instructions, with no LDS
+// round trip. Every lane receives op(own, partner); each op here is
+// commutative, so the result is bit-identical to op(x, shuffle_xor(x, d)).
+__device__ __forceinline__ float add_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     v = max(v, dpp_u32<kDppQuadXor1>(v));

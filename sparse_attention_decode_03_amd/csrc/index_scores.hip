@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 #pragma unroll
         for (int v = 0; v < 16; v++)
             part = __builtin_fmaf(wv[v], __builtin_fmaxf(acc[v], 0.0f), part);
-        const float tot = part + __shfl_xor(part, 32, kWave);
+        const float tot = add_xor32(part);
         const int t = t0 + col0 + (lane & 31);
         if (hl == 0 && t < L)
             scores[(int64_t)r * stride + t] = tot;

@@ -202,8 +202,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                 z[j] = rowidx[step * kStep + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
                 mx = __builtin_fmaxf(mx, z[j]);
             }
-            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            mx = max_xor32(max_xor16(mx));
             // The reference max moves only when the step's max exceeds it by
             // more than kRescaleSlack (log2 units): then p <= 2^kRescaleSlack,
             // so fp32 sums and bf16 probabilities stay well scaled, and O is
@@ -246,8 +245,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
             __syncthreads();
         }
         // per-head (m, l): the four lanes of a head hold shares of l
-        const float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-        const float l_all = l_tot + __shfl_xor(l_tot, 32, kWave);
+        const float l_all = add_xor32(add_xor16(l_run));
         if (active && g == 0) {
             mlds[hl] = float2{m_run, l_all};
             if (nch > 1) {
