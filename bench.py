@@ -173,6 +173,32 @@ def main() -> int:
         torch.cuda.synchronize()
         warm = time.perf_counter() - wt0
 
+        # per-step spread: the same rotating steps, each between HIP events
+        # on the stream (a separate pass, so the timed loop above carries no
+        # event records)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
+            run(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        step_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
+
+        # a plain streaming read on the same device (torch's row sums over
+        # 2 GiB of bf16 in 4096-wide rows: reads 2 GiB, writes 1 MiB), the
+        # practical HBM read ceiling the index kernel is held to
+        big = torch.ones(1 << 30, dtype=torch.bfloat16, device="cuda").view(-1, 4096)
+        big.sum(1)
+        sa = torch.cuda.Event(enable_timing=True)
+        sb = torch.cuda.Event(enable_timing=True)
+        sa.record(stream)
+        for _ in range(5):
+            big.sum(1)
+        sb.record(stream)
+        torch.cuda.synchronize()
+        read_ceiling = 5 * big.numel() * 2 / (sa.elapsed_time(sb) * 1e-3) / 1e9
+        del big
+
         # dominant kernel: the index-score pass, launched back to back on
         # rotating replicas (cold keys, as in the timed steps) between one
         # pair of HIP events on the stream it runs on; the mean per launch
@@ -227,6 +253,10 @@ def main() -> int:
             "achieved_GBs": ab["total"] / (ms * 1e-3) / 1e9,
             "frac": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
+        "step_us": {"p10": float(np.percentile(step_us, 10)), "p50": float(np.median(step_us)),
+                    "p90": float(np.percentile(step_us, 90))},
+        "hbm_read_ceiling": {"GBs": read_ceiling, "kernel": "torch row sums over 2 GiB bf16",
+                             "index_frac_of_ceiling": achieved / read_ceiling},
         "warm_value": args.steps / warm,
         "input_gen_s": round(t_gen, 2),
     }
