@@ -253,6 +253,7 @@ def main() -> int:
             "achieved_GBs": ab["total"] / (ms * 1e-3) / 1e9,
             "frac": ab["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
+        "rows_per_s": args.steps / elapsed * int(inputs["seq_lens"].shape[0]),
         "step_us": {"p10": float(np.percentile(step_us, 10)), "p50": float(np.median(step_us)),
                     "p90": float(np.percentile(step_us, 90))},
         "hbm_read_ceiling": {"GBs": read_ceiling, "kernel": "torch row sums over 2 GiB bf16",
