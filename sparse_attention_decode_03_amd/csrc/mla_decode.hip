@@ -69,9 +69,13 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // Each head's arithmetic is the same whichever heads share its workgroup (a
 // head whose reference did not move rescales by exactly 1), so G changes
 // where the work runs, never a result.
+// kv carries no __restrict__: loads through a const restrict pointer count as
+// invariant, and the compiler then sinks the prologue's gathers past the
+// barriers to just before their use, where the stage waits a full memory
+// round trip for them.
 template <int G>
 __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
-    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+    const uint16_t *__restrict__ q, const uint8_t *kv,
     const int32_t *__restrict__ bt, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ sel, uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml,
     uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
