@@ -148,17 +148,18 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         // ================= scoring waves: QK + online softmax =================
         const int hl = wave * 16 + n16; // this lane's head within the group
         const bool active = wave < kHt && wave * 16 < nh;
-        // query of head hl, latent dims 32 ks + 8 g .. +7 (the B operand);
-        // branch-free, a missing head loads head H-1 and is zeroed
+        // query of head hl, latent dims 32 ks + 8 g .. +7 (the B operand).
+        // A lane past the group's last head scores with head H-1's query:
+        // its results are never stored, and it cannot change another head's
+        // (its reference moves exactly when head H-1's does, and an unmoved
+        // head rescales by exactly 1). Nothing reads the loads before the
+        // first product, so they stay in flight through the prologue.
         u32x4 qr[16];
         if (active) {
             const uint16_t *qrow = q + ((int64_t)r * H + min(h0 + hl, H - 1)) * kLat + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < 16; ks++) {
+            for (int ks = 0; ks < 16; ks++)
                 qr[ks] = *(const u32x4 *)(qrow + 32 * ks);
-                if (h0 + hl >= H)
-                    qr[ks] = u32x4{0u, 0u, 0u, 0u};
-            }
         }
         float m_run = kNegInf; // reference max of the log2-domain logits (head hl)
         float l_run = 0.0f;    // this lane's share of sum exp2(z - m_run)
