@@ -474,8 +474,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 }
 
 // Fold the per-chunk partials of every (row, head) in chunk order.
-__global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ part_o,
-                                                   const float2 *__restrict__ part_ml,
+// (the partial pointers carry no __restrict__, so the first batch's loads are
+// not sunk below the row-length test: loads through const restrict pointers
+// count as invariant and move freely)
+__global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *part_o,
+                                                   const float2 *part_ml,
                                                    const int32_t *__restrict__ seq_lens,
                                                    uint16_t *__restrict__ out, int H, int top_k,
                                                    int max_len, int nch_max, int hg_count,
@@ -483,35 +486,43 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *__restrict__ 
 {
     const int r = blockIdx.y;
     const int h = blockIdx.x;
-    const int L = min(max(seq_lens[r], 0), max_len);
-    const int n = min(top_k, L);
-    const int nch = (n + kAttChunk - 1) / kAttChunk;
-    if (nch <= 1)
-        return;
     const int hg = h / G;
     const int hl = h % G;
     const int d = threadIdx.x * 4;
-    float m_acc = kNegInf, l_acc = 0.0f;
-    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int64_t pbase = ((int64_t)r * hg_count + hg) * nch_max * G + hl;
     // partials are loaded in unrolled batches (independent loads in flight),
     // then folded strictly in chunk order; straight-line code with selects,
     // so the batch stays in registers. A batch is the chunk count of a row
     // at top_k = 2048 (8 x 256 slots): a larger one re-reads the last chunk
     // (measured: 16 cost 3.5 us per step at 64 x 16.4k)
     constexpr int kB = 8;
-    for (int c0 = 0; c0 < nch; c0 += kB) {
-        float2 ml[kB];
-        floatx4 ov[kB];
+    float2 ml[kB];
+    floatx4 ov[kB];
+    // branch-free: chunks past the last re-read it (and are not folded)
+    auto load_batch = [&](int c0, int last) {
 #pragma unroll
         for (int k = 0; k < kB; k++) {
-            // branch-free: chunks past the row's last re-read its last one
-            const int64_t pi =
-                (((int64_t)r * hg_count + hg) * nch_max + min(c0 + k, nch - 1)) * G + hl;
+            const int64_t pi = pbase + (int64_t)min(c0 + k, last) * G;
             ml[k] = part_ml[pi];
             const u32x2 pk = *(const u32x2 *)(part_o + pi * kLat + d);
             ov[k] = floatx4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
                             __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)};
         }
+    };
+    // the first batch goes out before the row's chunk count is known (every
+    // chunk up to nch_max has its place in the workspace)
+    load_batch(0, nch_max - 1);
+    __asm__ volatile("" ::: "memory"); // those loads stay ahead of the length load and test
+    const int L = min(max(seq_lens[r], 0), max_len);
+    const int n = min(top_k, L);
+    const int nch = (n + kAttChunk - 1) / kAttChunk;
+    if (nch <= 1)
+        return;
+    float m_acc = kNegInf, l_acc = 0.0f;
+    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = 0; c0 < nch; c0 += kB) {
+        if (c0 > 0)
+            load_batch(c0, nch - 1);
 #pragma unroll
         for (int k = 0; k < kB; k++) {
             const float m_new = __builtin_fmaxf(m_acc, ml[k].x);
