@@ -107,7 +107,6 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int nch = (n + kAttChunk - 1) / kAttChunk;
     const int h0 = hg * G;         // first head of the group
     const int nh = min(G, H - h0); // heads of the group that exist
-    const int mt_count = (nh + 15) / 16;   // 16-head tiles that exist
 
     if (n == 0) {
         if (c == 0) {
