@@ -143,6 +143,38 @@ def topk(scores, seq_lens, top_k: int) -> np.ndarray:
     return sel
 
 
+def pooled_select(pool_scores, seq_lens, kp: int, select_k: int) -> np.ndarray:
+    """Pooled selection and its expansion to tokens: sel [R, select_k*kp + kp - 1]
+    int32, -1 padded.
+
+    Follows the doc of the prefill row-group selector on the glm5next_dsa
+    layer.rs source page: pool p (tokens p*kp .. p*kp + kp - 1) is a candidate
+    of a row only when it is complete and its last token is visible to the
+    row's query, i.e. p < (q_pos + 1) / kp = L // kp; the row takes
+    row_select_k = min(select_k, L // kp) pools under the total order (score
+    descending, pool index ascending); the selected pools expand to their kp
+    tokens each, and the row's visible tail (tokens L // kp * kp .. L - 1, the
+    incomplete pool) is written from slot row_select_k * kp on.
+    Readings: pools expand in ascending pool order (as the per-token ids are
+    ascending); the pool scores are an input (how the pages form them from
+    the gate and the positional term is not on the pages)."""
+    seq_lens = _c(seq_lens, np.int32)
+    R = seq_lens.shape[0]
+    width = select_k * kp + kp - 1
+    out = np.full((R, width), -1, dtype=np.int32)
+    for r in range(R):
+        L = int(seq_lens[r])
+        pvis = L // kp
+        rsk = min(select_k, pvis)
+        tokens = []
+        if pvis > 0:
+            pools = topk_row(np.asarray(pool_scores[r], dtype=np.float64)[:pvis], pvis, select_k)[:rsk]
+            tokens = [int(p) * kp + i for p in pools for i in range(kp)]
+        tokens += list(range(pvis * kp, L))
+        out[r, :len(tokens)] = tokens
+    return out
+
+
 def mla_decode(q, kv_cache, block_tables, seq_lens, sel, kv_scale: float, sm_scale: float,
                rows_per_seq: int = 1) -> np.ndarray:
     """out [R, H, Dl] float64."""

@@ -1,0 +1,87 @@
+"""Pins of the oracle's pooled selection (doc of the prefill row-group selector,
+glm5next_dsa/layer.rs source page): candidacy, total order, expansion and the
+per-row tail base. CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def dominance_ok(scores, pools, pvis):
+    """Every selected visible pool comes before every unselected one under
+    (score descending, pool ascending)."""
+    sel = set(int(p) for p in pools)
+    for p in sel:
+        for q in range(pvis):
+            if q in sel:
+                continue
+            if not (scores[p] > scores[q] or (scores[p] == scores[q] and p < q)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("select_k", [1, 3, 8, 40])
+def test_one_token_pools_are_the_per_token_selection(select_k):
+    rng = np.random.default_rng(7)
+    scores = rng.standard_normal((6, 50))
+    lens = np.array([50, 1, 7, 23, 49, 8], np.int32)
+    got = oracle.pooled_select(scores, lens, 1, select_k)
+    want = oracle.topk(scores, lens, select_k)
+    assert got.shape == want.shape
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("kp", [2, 3, 4, 16])
+def test_selected_pools_dominate_the_rest(kp):
+    rng = np.random.default_rng(kp)
+    # integer scores in a small range: many exact ties
+    scores = rng.integers(-2, 3, size=(8, 40)).astype(np.float64)
+    lens = rng.integers(1, 40 * kp + 1, size=8).astype(np.int32)
+    for select_k in (1, 4, 11):
+        out = oracle.pooled_select(scores, lens, kp, select_k)
+        for r in range(8):
+            L = int(lens[r])
+            pvis = L // kp
+            rsk = min(select_k, pvis)
+            head = out[r, :rsk * kp].reshape(rsk, kp) if rsk else np.zeros((0, kp), int)
+            pools = head[:, 0] // kp
+            # each pool expands to its kp consecutive tokens, pools ascending
+            assert (head == pools[:, None] * kp + np.arange(kp)[None, :]).all()
+            assert (np.diff(pools) > 0).all()
+            assert (pools < pvis).all()
+            assert dominance_ok(scores[r], pools, pvis)
+            # the visible tail follows at the row's own base, then padding
+            tail = out[r, rsk * kp: rsk * kp + (L - pvis * kp)]
+            np.testing.assert_array_equal(tail, np.arange(pvis * kp, L))
+            assert (out[r, rsk * kp + (L - pvis * kp):] == -1).all()
+
+
+def test_invisible_and_incomplete_pools_are_never_selected():
+    kp = 4
+    scores = np.zeros((1, 10))
+    scores[0, 5:] = 1e9          # pools 5.. are past the row's query
+    out = oracle.pooled_select(scores, [22], kp, 3)   # pools 0..4 complete, tail 20, 21
+    assert out[0, :12].max() < 20 and set(out[0, :12] // kp) <= {0, 1, 2, 3, 4}
+    np.testing.assert_array_equal(out[0, 12:14], [20, 21])
+
+
+def test_rows_shorter_than_a_pool_keep_only_their_tail():
+    out = oracle.pooled_select(np.ones((2, 4)), [3, 1], 4, 2)
+    np.testing.assert_array_equal(out[0, :3], [0, 1, 2])
+    np.testing.assert_array_equal(out[1, :1], [0])
+    assert (out[0, 3:] == -1).all() and (out[1, 1:] == -1).all()
+
+
+def test_every_visible_pool_selected_gives_every_token():
+    rng = np.random.default_rng(3)
+    out = oracle.pooled_select(rng.standard_normal((1, 9)), [37], 4, 9)  # 9 pools visible
+    np.testing.assert_array_equal(out[0, :37], np.arange(37))
+    assert (out[0, 37:] == -1).all()
+
+
+def test_the_tail_base_is_the_row_own_selection_size():
+    # select_k = 6 but the row sees only 2 complete pools: the tail starts at
+    # slot 2 * kp, not 6 * kp (the pages' per-row correction)
+    out = oracle.pooled_select(np.arange(8.0)[None, :], [11], 4, 6)
+    np.testing.assert_array_equal(out[0, :11], np.arange(11))
+    assert (out[0, 11:] == -1).all()
