@@ -10,6 +10,8 @@
  *   dsa_mla_decode    NoPE MLA attention of a latent-absorbed query over the
  *                     selected rows of an FP8 paged 512-wide latent cache
  *   dsa_decode_k      index -> select -> attend for S sequences x K rows
+ *   dsa_topk_select_pooled  the same selection over pools of kp tokens,
+ *                     expanded back to token ids
  *
  * Sources: the pages describing the GLM-5.3 DSA layer of the spark_model
  * crate -- the "spark_model/layers/glm5next_dsa/layer.rs" source page (cited
@@ -182,6 +184,36 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w,
                  const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
                  float sm_scale, float *scores, int32_t *sel, void *out, void *ws,
                  size_t ws_bytes, void *stream);
+
+/*
+ * Pooled selection (the selector of the pages' own layer, on pools of kp
+ * consecutive tokens) and its expansion back to token ids. layer.rs, doc of
+ * the prefill row-group selector: a pool is a candidate of row r only when it
+ * is complete and its last token is visible to the row's query, so the row
+ * sees pools [0, L_r / kp); it takes row_select_k = min(top_k, L_r / kp)
+ * pools under the total order (score descending, pool index ascending); the
+ * selected pools expand to their kp tokens, and the row's visible tail (the
+ * incomplete pool, tokens L_r / kp * kp .. L_r - 1) goes from slot
+ * row_select_k * kp on. With kp = 1 this is dsa_topk_select.
+ *   shape->top_k   pools to select (select_k); shape->max_len the token ceiling
+ *   kp             tokens per pool, in [1, 1024]
+ *   pool_scores    [R, dsa_pool_score_stride(shape, kp)] fp32, entries
+ *                  [0, L_r / kp) read. How the pages form pool scores (their
+ *                  gate and positional terms) is not on the pages: the
+ *                  caller supplies them.
+ *   seq_lens       [R] int32
+ *   sel            [R, top_k * kp + kp - 1] int32 (output): the selected
+ *                  pools' tokens in ascending pool order, then the tail, then
+ *                  -1
+ *   ws             >= dsa_pooled_workspace_bytes(shape, kp) bytes
+ * Refusals: as dsa_topk_select; kp outside [1, 1024] is EUNSUPPORTED. The
+ * helpers return 0 for a refused shape or kp.
+ */
+size_t dsa_pooled_workspace_bytes(const dsa_shape *shape, int32_t kp);
+size_t dsa_pool_score_stride(const dsa_shape *shape, int32_t kp);
+int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool_scores,
+                           const int32_t *seq_lens, int32_t *sel, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /*
  * The cache-write side that feeds the path (the step before it): row r

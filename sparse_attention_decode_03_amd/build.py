@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["dsa_abi.hip", "index_scores.hip", "topk_select.hip", "mla_decode.hip",
-           "cache_write.hip"]
+           "cache_write.hip", "pooled.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -103,6 +103,41 @@ int launched(int rc, const char *what)
     return DSA_OK;
 }
 
+constexpr int kMaxPoolTokens = 1024; // kp above this is refused
+
+// The pooled selection's shapes and workspace: the token shape's selector run
+// on pools (max_len = max(1, max_len / kp) pools, top_k = select_k pools),
+// then per-row pool counts and the selected pools.
+struct PooledLayout {
+    dsa::LaunchShape ls_pool;
+    dsa::Workspace wl;
+    size_t pool_lens, sel_pools, total;
+    int max_len; // the token ceiling
+    bool any_pool;
+};
+
+int pooled_layout(const dsa_shape *shape, int32_t kp, PooledLayout *pl)
+{
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if (kp < 1 || kp > kMaxPoolTokens)
+        return fail(DSA_EUNSUPPORTED, "pool size %d outside [1, %d]", kp, kMaxPoolTokens);
+    pl->max_len = ls.max_len;
+    pl->any_pool = ls.max_len >= kp;
+    pl->ls_pool = ls;
+    pl->ls_pool.max_len = ls.max_len / kp > 0 ? ls.max_len / kp : 1;
+    pl->wl = dsa::workspace_layout(pl->ls_pool);
+    size_t off = pl->wl.total;
+    pl->pool_lens = off;
+    off = align256(off + (size_t)ls.num_rows * sizeof(int32_t));
+    pl->sel_pools = off;
+    off = align256(off + (size_t)ls.num_rows * ls.top_k * sizeof(int32_t));
+    pl->total = off;
+    return DSA_OK;
+}
+
 } // namespace
 
 namespace dsa {
@@ -156,6 +191,45 @@ size_t dsa_score_stride(const dsa_shape *shape)
     if (check_shape(shape, &ls) != DSA_OK)
         return 0;
     return (size_t)dsa::score_stride(ls);
+}
+
+size_t dsa_pooled_workspace_bytes(const dsa_shape *shape, int32_t kp)
+{
+    PooledLayout pl;
+    if (pooled_layout(shape, kp, &pl) != DSA_OK)
+        return 0;
+    return pl.total;
+}
+
+size_t dsa_pool_score_stride(const dsa_shape *shape, int32_t kp)
+{
+    PooledLayout pl;
+    if (pooled_layout(shape, kp, &pl) != DSA_OK)
+        return 0;
+    return (size_t)dsa::score_stride(pl.ls_pool);
+}
+
+int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool_scores,
+                           const int32_t *seq_lens, int32_t *sel, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    g_err[0] = 0;
+    PooledLayout pl;
+    int rc;
+    if ((rc = pooled_layout(shape, kp, &pl)) != DSA_OK)
+        return rc;
+    if ((rc = check_ptr(pool_scores, "pool_scores")) || (rc = check_ptr(seq_lens, "seq_lens")) ||
+        (rc = check_ptr(sel, "sel")))
+        return rc;
+    if (check_ptr(ws, "ws") != DSA_OK)
+        return fail(DSA_EWORKSPACE, "workspace is NULL or not 16-byte aligned");
+    if (ws_bytes < pl.total)
+        return fail(DSA_EWORKSPACE, "workspace of %zu bytes is below the %zu this shape needs",
+                    ws_bytes, pl.total);
+    return launched(dsa::launch_select_pooled(pl.ls_pool, pl.max_len, kp, pool_scores, seq_lens,
+                                              sel, (char *)ws, pl.wl, pl.pool_lens, pl.sel_pools,
+                                              pl.any_pool, (hipStream_t)stream),
+                    "select_pooled");
 }
 
 size_t dsa_bt_entries_needed(size_t seq_len, size_t k, size_t block_size)

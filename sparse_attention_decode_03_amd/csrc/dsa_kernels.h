@@ -69,6 +69,15 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
                   hipStream_t stream);
+// Pooled selection of pool_scores [R][score_stride(ls_pool)] over per-row
+// pool counts L_r / kp, expanded to token ids in sel [R][top_k * kp + kp - 1].
+// ls_pool is the token shape with max_len = max(1, max_len / kp); pool counts
+// and selected pools live in the workspace at the given offsets; any_pool
+// false (max_len < kp) skips the selection (every row keeps its tail only).
+int launch_select_pooled(const LaunchShape &ls_pool, int max_len, int kp, const float *pool_scores,
+                         const int32_t *seq_lens, int32_t *sel, char *ws, const Workspace &wl,
+                         size_t pool_lens_off, size_t sel_pools_off, bool any_pool,
+                         hipStream_t stream);
 int launch_cache_write(const LaunchShape &ls, const uint16_t *kv_a, const uint16_t *latent_w,
                        const uint16_t *k_proj, const uint16_t *k_w, const uint16_t *k_b,
                        const int32_t *seq_lens, const int32_t *block_tables, float eps,

@@ -30,6 +30,9 @@ EXPORTS = (
     "dsa_mla_decode",
     "dsa_decode_k",
     "dsa_cache_write",
+    "dsa_topk_select_pooled",
+    "dsa_pooled_workspace_bytes",
+    "dsa_pool_score_stride",
     "dsa_score_stride",
     "dsa_bt_entries_needed",
     "dsa_last_error",
@@ -109,6 +112,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_cache_write.restype = i32
     lib.dsa_score_stride.argtypes = [S]
     lib.dsa_score_stride.restype = sz
+    lib.dsa_pooled_workspace_bytes.argtypes = [S, i32]
+    lib.dsa_pooled_workspace_bytes.restype = sz
+    lib.dsa_pool_score_stride.argtypes = [S, i32]
+    lib.dsa_pool_score_stride.restype = sz
+    lib.dsa_topk_select_pooled.argtypes = [S, i32, P, P, P, P, sz, P]
+    lib.dsa_topk_select_pooled.restype = i32
     lib.dsa_bt_entries_needed.argtypes = [sz, sz, sz]
     lib.dsa_bt_entries_needed.restype = sz
     lib.dsa_last_error.argtypes = []
@@ -167,6 +176,23 @@ def topk_select(shape: Shape, scores, seq_lens, sel, ws, ws_bytes: Optional[int]
     nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(load().dsa_topk_select(ctypes.byref(shape), _ptr(scores), _ptr(seq_lens), _ptr(sel),
                                   _ptr(ws), nb, _stream(stream)))
+
+
+def pooled_workspace_bytes(shape: Shape, kp: int) -> int:
+    return int(load().dsa_pooled_workspace_bytes(ctypes.byref(shape), kp))
+
+
+def pool_score_stride(shape: Shape, kp: int) -> int:
+    """Row stride (floats) of a pool-scores buffer for `shape` and pools of kp tokens."""
+    return int(load().dsa_pool_score_stride(ctypes.byref(shape), kp))
+
+
+def topk_select_pooled(shape: Shape, kp: int, pool_scores, seq_lens, sel, ws,
+                       ws_bytes: Optional[int] = None, stream=None) -> None:
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(load().dsa_topk_select_pooled(ctypes.byref(shape), kp, _ptr(pool_scores),
+                                         _ptr(seq_lens), _ptr(sel), _ptr(ws), nb,
+                                         _stream(stream)))
 
 
 def mla_decode(shape: Shape, q, kv_cache, block_tables, seq_lens, sel, kv_scale: float,

@@ -95,3 +95,15 @@ def test_bt_entries_needed_matches_the_pages_trim_tests():
         n = dsa.bt_entries_needed(seq_len, k, bs)
         highest = max(seq_len + k - 1, 0) // bs
         assert highest < n
+
+
+def test_pooled_helpers_size_by_pools_and_refuse_bad_pool_sizes():
+    sh = good_shape()
+    # pool scores rows are max_len / kp pools, rounded up to 64 floats
+    assert dsa.pool_score_stride(sh, 1) == dsa.score_stride(sh)
+    assert dsa.pool_score_stride(sh, 4) == (16388 // 4 + 63) // 64 * 64
+    assert dsa.pooled_workspace_bytes(sh, 4) > 0
+    assert dsa.pooled_workspace_bytes(sh, 0) == 0
+    assert dsa.pooled_workspace_bytes(sh, 1025) == 0
+    # a pool longer than every row still has a layout (rows keep their tails)
+    assert dsa.pooled_workspace_bytes(good_shape(max_len=100, k_capacity=100), 512) > 0

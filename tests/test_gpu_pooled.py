@@ -1,0 +1,110 @@
+"""GPU parity of the pooled selection (dsa_topk_select_pooled, through the C
+ABI) against the oracle: pool candidacy, total order, expansion and tail
+placement, and attention over the expanded ids."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_03_amd import dsa
+from sparse_attention_decode_03_amd import workloads as wl
+
+from gpu_common import ATT_ATOL, bf16_codes_to_f64, small
+
+pytestmark = pytest.mark.gpu
+
+
+def run_pooled(lens, kp, select_k, scores_fn, max_len=None, seed=0):
+    lens = np.asarray(lens, np.int32)
+    R = lens.shape[0]
+    max_len = int(lens.max()) if max_len is None else max_len
+    sh = dsa.Shape(num_seqs=R, rows_per_seq=1, num_heads=64, latent_dim=512, index_heads=32,
+                   index_dim=128, top_k=select_k, page_size=64, max_len=max_len,
+                   k_capacity=max_len, max_blocks_per_seq=(max_len + 63) // 64 + 1,
+                   num_pages=R * ((max_len + 63) // 64 + 1))
+    stride = dsa.pool_score_stride(sh, kp)
+    rng = np.random.default_rng(seed)
+    scores = np.full((R, stride), np.nan, np.float32)   # entries past a row's pools are never read
+    for r in range(R):
+        npool = int(lens[r]) // kp
+        scores[r, :npool] = scores_fn(rng, npool)
+    width = select_k * kp + kp - 1
+    print(f"pooled: R={R} kp={kp} select_k={select_k} max_len={max_len}", flush=True)
+    d_scores = torch.from_numpy(scores).cuda()
+    d_lens = torch.from_numpy(lens).cuda()
+    d_sel = torch.full((R, width), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.pooled_workspace_bytes(sh, kp), dtype=torch.uint8, device="cuda")
+    dsa.topk_select_pooled(sh, kp, d_scores, d_lens, d_sel, ws)
+    torch.cuda.synchronize()
+    got = d_sel.cpu().numpy()
+    want = oracle.pooled_select(np.nan_to_num(scores, nan=0.0).astype(np.float64), lens, kp,
+                                select_k)
+    np.testing.assert_array_equal(got, want)
+    return sh, scores, lens, got
+
+
+normal = lambda rng, n: rng.standard_normal(n).astype(np.float32)
+ties = lambda rng, n: rng.integers(-2, 3, size=n).astype(np.float32)
+
+
+@pytest.mark.parametrize("kp,select_k,lens,fn", [
+    (4, 64, [1000, 3, 4, 257, 640], normal),
+    (16, 32, [5000, 15, 16, 700, 4096], ties),
+    (64, 64, [131072, 8192, 100], normal),
+    (4, 2048, [131072, 65536, 9000, 8191], normal),
+    (2, 512, [20000, 1023, 1024, 1025], ties),
+])
+def test_pooled_selection_matches_the_oracle(kp, select_k, lens, fn):
+    run_pooled(lens, kp, select_k, fn, seed=kp * 7 + select_k)
+
+
+def test_one_token_pools_equal_the_token_selector():
+    lens = np.array([3000, 2048, 17, 9000], np.int32)
+    sh, scores, lens, got = run_pooled(lens, 1, 2048, normal, seed=5)
+    d_sel = torch.empty((4, 2048), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.workspace_bytes(sh), dtype=torch.uint8, device="cuda")
+    dsa.topk_select(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(lens).cuda(), d_sel, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, d_sel.cpu().numpy())
+
+
+def test_pools_longer_than_every_row_keep_only_the_tails():
+    run_pooled([5, 100, 1], 128, 8, normal, max_len=100 + 5)
+
+
+def test_attention_over_pooled_ids_matches_the_oracle():
+    # a seeded decode workload; its own scores stand in for pool scores of kp
+    # = 8 (one per pool: the first token's), and the expanded ids feed the
+    # attention through the C ABI
+    kp, select_k = 8, 64
+    inputs = small(num_seqs=2, rows_per_seq=1, lengths="ragged", lo=900, hi=2500, top_k=2048,
+                   seed=31)
+    lens = inputs["seq_lens"]
+    R = lens.shape[0]
+    sh_pool = dsa.shape_of(inputs, top_k=select_k)
+    stride = dsa.pool_score_stride(sh_pool, kp)
+    rng = np.random.default_rng(31)
+    pool_scores = rng.standard_normal((R, stride)).astype(np.float32)
+    width = select_k * kp + kp - 1
+    d_sel = torch.empty((R, width), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.pooled_workspace_bytes(sh_pool, kp), dtype=torch.uint8, device="cuda")
+    step = dsa.DeviceStep(inputs, top_k=width)
+    dsa.topk_select_pooled(sh_pool, kp, torch.from_numpy(pool_scores).cuda(), step.seq_lens,
+                           d_sel, ws)
+    dsa.mla_decode(step.shape, step.q, step.kv_cache, step.block_tables, step.seq_lens, d_sel,
+                   step.kv_scale, step.sm_scale, step.out, step.ws)
+    torch.cuda.synchronize()
+    sel = d_sel.cpu().numpy()
+    np.testing.assert_array_equal(sel, oracle.pooled_select(pool_scores.astype(np.float64), lens,
+                                                            kp, select_k))
+    out = bf16_codes_to_f64(step.out.cpu().numpy().view(np.uint16))
+    # the oracle attends over exactly the ids a row selected (its valid prefix);
+    # the kernel skips the -1 slots past it
+    for r in range(R):
+        cnt = int((sel[r] >= 0).sum())
+        assert (sel[r, :cnt] >= 0).all() and (sel[r, cnt:] == -1).all()
+        ref = oracle.mla_decode(inputs["q"][r:r + 1], inputs["kv_cache"],
+                                inputs["block_tables"][r:r + 1], lens[r:r + 1],
+                                np.ascontiguousarray(sel[r:r + 1, :cnt]), inputs["kv_scale"],
+                                inputs["sm_scale"], 1)
+        assert np.abs(out[r] - ref[0]).max() <= ATT_ATOL, r
