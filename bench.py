@@ -92,6 +92,47 @@ def cpu_baseline(inputs: dict, budget_s: float = 12.0) -> dict:
             "rows_per_seq": K}
 
 
+def bench_pooled(args, wlk, inputs: dict, sh) -> int:
+    """Pooled selection alone at the workload's rows and lengths: seeded
+    N(0,1) pool scores resident in HBM, top_k / kp pools per row; prints one
+    JSON line (calls/s and the selected ids per second)."""
+    import torch
+    from sparse_attention_decode_03_amd import dsa
+    kp = args.pooled_kp
+    select_k = max(1, wlk.top_k // kp)
+    psh = dsa.shape_of(inputs, top_k=select_k)
+    R = psh.num_rows
+    stride = dsa.pool_score_stride(psh, kp)
+    rng = np.random.default_rng(1234)
+    scores = torch.from_numpy(rng.standard_normal((R, stride)).astype(np.float32)).cuda()
+    lens = torch.from_numpy(inputs["seq_lens"]).cuda()
+    width = select_k * kp + kp - 1
+    sel = torch.empty((R, width), dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.pooled_workspace_bytes(psh, kp), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            dsa.topk_select_pooled(psh, kp, scores, lens, sel, ws, stream=stream)
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        ea.record(stream)
+        for _ in range(args.steps):
+            dsa.topk_select_pooled(psh, kp, scores, lens, sel, ws, stream=stream)
+        eb.record(stream)
+        torch.cuda.synchronize()
+    ms = ea.elapsed_time(eb) / args.steps
+    n_sel = int(np.minimum(inputs["seq_lens"] // kp, select_k).sum() * kp
+                + (inputs["seq_lens"] % kp).sum())
+    print(json.dumps({"metric": "pooled selection calls/sec", "value": 1e3 / ms, "unit": "calls/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_call": ms,
+                      "higher_is_better": True, "data": "synthetic",
+                      "config": {"workload": wlk.name, "rows": R, "pool_tokens": kp,
+                                 "pools_per_row": select_k,
+                                 "max_pools": int(inputs["max_len"]) // kp},
+                      "selected_ids_per_s": n_sel * 1e3 / ms}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +144,9 @@ def main() -> int:
                     help="input copies the steps rotate through (1 = warm caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--index-launches", type=int, default=50)
+    ap.add_argument("--pooled-kp", type=int, default=0,
+                    help="time the pooled selection (pools of this many tokens, top_k / kp "
+                         "pools per row, synthetic pool scores) instead of the decode step")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the index kernel and a plain 256 MiB device copy a few "
                          "times each (for rocprofv3 counter passes), then exit")
@@ -134,6 +178,9 @@ def main() -> int:
         dsa.decode_k(sh, step.q_idx, step.w, keys[i % nrep], step.q, pools[i % nrep],
                      step.block_tables, step.seq_lens, step.kv_scale, step.sm_scale,
                      step.scores, step.sel, step.out, step.ws, stream=stream)
+
+    if args.pooled_kp > 0:
+        return bench_pooled(args, wlk, inputs, sh)
 
     if args.traffic_probe:
         # HBM counters read per dispatch: the index kernel, and a plain copy of
