@@ -56,6 +56,9 @@ def _load() -> ctypes.CDLL:
     lib.oracle_mla_decode.argtypes = [i32, i32, i32, i32, P, P, i64, i32, P, i64, P, P, i64,
                                       dbl, dbl, P]
     lib.oracle_mla_decode.restype = i32
+    lib.oracle_mla_decode_abs.argtypes = [i32, i32, i32, i32, P, P, i64, i32, P, i64, P, P,
+                                          i64, dbl, dbl, P]
+    lib.oracle_mla_decode_abs.restype = i32
     lib.oracle_softmax_weights.argtypes = [i32, i32, i32, i32, i32, P, P, i64, i32, P, i64, P,
                                            P, i64, dbl, dbl, P]
     lib.oracle_softmax_weights.restype = i32
@@ -192,6 +195,27 @@ def mla_decode(q, kv_cache, block_tables, seq_lens, sel, kv_scale: float, sm_sca
                                    _p(block_tables), block_tables.shape[1], _p(seq_lens),
                                    _p(sel), top_k, float(kv_scale), float(sm_scale), _p(out))
     _check(rc, "oracle_mla_decode")
+    return out
+
+
+def mla_decode_abs(q, kv_cache, block_tables, seq_lens, sel, kv_scale: float, sm_scale: float,
+                   rows_per_seq: int = 1) -> np.ndarray:
+    """Error scale [R, H, Dl] float64: sum_j p_j |c_j| with mla_decode's weights
+    and rows (a relative rounding u of every weight or partial sum moves the
+    output by at most u times this)."""
+    q = _c(q, np.uint16)
+    kv_cache = _c(kv_cache, np.uint8)
+    block_tables = _c(block_tables, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    sel = _c(sel, np.int32)
+    R, H, Dl = q.shape
+    num_pages, ps, _ = kv_cache.shape
+    top_k = sel.shape[1]
+    out = np.zeros((R, H, Dl), dtype=np.float64)
+    rc = _load().oracle_mla_decode_abs(R, rows_per_seq, H, Dl, _p(q), _p(kv_cache), num_pages, ps,
+                                       _p(block_tables), block_tables.shape[1], _p(seq_lens),
+                                       _p(sel), top_k, float(kv_scale), float(sm_scale), _p(out))
+    _check(rc, "oracle_mla_decode_abs")
     return out
 
 

@@ -331,6 +331,91 @@ int oracle_mla_decode(int R, int K, int H, int Dl,
     return status;
 }
 
+/*
+ * Error scale of the attention output, for the parity tests' second bound:
+ *   scale[r, h, d] = sum_j p_j * |c_j[d]|
+ * with the same weights p and rows c_j as oracle_mla_decode (the output with
+ * every value replaced by its magnitude). A relative rounding of every p_j
+ * (or of every partial sum over a subset of the j) by at most u moves
+ * out[r, h, d] by at most u * scale[r, h, d]. Same arguments, refusals and
+ * layout as oracle_mla_decode.
+ * Parity: pinned (the same weights through torch's casts and softmax on the
+ * dense logits; equal to |out| where a column's values share one sign).
+ */
+int oracle_mla_decode_abs(int R, int K, int H, int Dl,
+                          const uint16_t *q, const uint8_t *kv_cache,
+                          int64_t num_pages, int page_size,
+                          const int32_t *block_tables, int64_t max_blocks,
+                          const int32_t *seq_lens, const int32_t *sel, int64_t top_k,
+                          double kv_scale, double sm_scale, double *scale)
+{
+    if (R < 0 || K < 1 || H < 1 || Dl < 1 || page_size < 1 || top_k < 1 || (R % K) != 0)
+        return ORACLE_EINVAL;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rh = 0; rh < (int64_t)R * H; rh++) {
+        int r = (int)(rh / H);
+        int s = r / K;
+        int64_t L = seq_lens[r];
+        int64_t n = L < top_k ? L : top_k;
+        double *o = scale + rh * Dl;
+        const uint16_t *qh = q + rh * Dl;
+        int rc = ORACLE_OK;
+        for (int d = 0; d < Dl; d++)
+            o[d] = 0.0;
+        if (n <= 0)
+            continue;
+        double *z = (double *)malloc(sizeof(double) * (size_t)n);
+        const uint8_t **rows = (const uint8_t **)malloc(sizeof(uint8_t *) * (size_t)n);
+        if (!z || !rows) {
+            rc = ORACLE_EINVAL;
+        } else {
+            for (int64_t j = 0; j < n && rc == ORACLE_OK; j++) {
+                int64_t t = sel[(int64_t)r * top_k + j];
+                if (t < 0 || t >= L || t / page_size >= max_blocks) {
+                    rc = ORACLE_EINVAL;
+                    break;
+                }
+                int64_t page = block_tables[(int64_t)s * max_blocks + t / page_size];
+                if (page < 0 || page >= num_pages) {
+                    rc = ORACLE_EINVAL;
+                    break;
+                }
+                rows[j] = kv_cache + (page * page_size + t % page_size) * (int64_t)Dl;
+                double dot = 0.0;
+                for (int d = 0; d < Dl; d++) {
+                    double c = kv_scale * oracle_e4m3fn_to_f64(rows[j][d]);
+                    if (isnan(c))
+                        rc = ORACLE_ENAN;
+                    dot += oracle_bf16_to_f64(qh[d]) * c;
+                }
+                z[j] = sm_scale * dot;
+            }
+            if (rc == ORACLE_OK) {
+                double zmax = z[0];
+                for (int64_t j = 1; j < n; j++)
+                    if (z[j] > zmax)
+                        zmax = z[j];
+                double denom = 0.0;
+                for (int64_t j = 0; j < n; j++)
+                    denom += exp(z[j] - zmax);
+                for (int64_t j = 0; j < n; j++) {
+                    double p = exp(z[j] - zmax) / denom;
+                    for (int d = 0; d < Dl; d++)
+                        o[d] += p * fabs(kv_scale * oracle_e4m3fn_to_f64(rows[j][d]));
+                }
+            }
+        }
+        free(z);
+        free(rows);
+        if (rc != ORACLE_OK) {
+#pragma omp critical
+            status = rc;
+        }
+    }
+    return status;
+}
+
 /* Softmax weights of one (row, head), for the sum-to-one pin: p[0..n_r). */
 int oracle_softmax_weights(int K, int H, int Dl, int r, int h,
                            const uint16_t *q, const uint8_t *kv_cache,

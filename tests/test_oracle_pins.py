@@ -418,3 +418,87 @@ def test_cache_write_slot_arithmetic_and_untouched_elsewhere():
                                 cache, keys)
     assert np.argwhere((c3 != cache).any(axis=2)).tolist() == [[0, 1]]
     assert np.argwhere((k3 != keys).any(axis=2)).tolist() == [[0, 5], [1, 1]]
+
+
+# ---------------------------------------------------------------------------
+# Softmax weights, the attention error scale and the end-to-end pipeline at
+# K > 1, each against torch's casts and softmax on the definitions.
+
+def torch_weights_and_rows(x, r, sel_row):
+    """Dense logits of row r over the ids sel_row (through torch's bf16 and
+    E4M3 casts), their softmax, and the dequantised rows."""
+    K, ps = x["rows_per_seq"], x["page_size"]
+    s = r // K
+    bt = x["block_tables"][s]
+    c = np.stack([dequant(x["kv_cache"][bt[t // ps], t % ps]) for t in sel_row]) * x["kv_scale"]
+    qd = bf16_to_f64(x["q"][r])                       # [H, Dl]
+    z = x["sm_scale"] * (qd @ c.T)                    # [H, n]
+    p = torch.softmax(torch.from_numpy(z), dim=-1).numpy()
+    return p, c
+
+
+def test_softmax_weights_equal_torch_softmax_of_the_dense_logits():
+    x = small_attend_inputs(50, L=37, top_k=9, H=4, Dl=32, ps=4, S=2, K=2)
+    x["seq_lens"] = np.array([37, 30, 33, 21], np.int32)
+    rng = np.random.default_rng(3)
+    sel = np.stack([np.sort(rng.choice(int(L), 9, replace=False)) for L in x["seq_lens"]]).astype(np.int32)
+    for r in range(4):
+        p_ref, _ = torch_weights_and_rows(x, r, sel[r])
+        for h in range(4):
+            p = oracle.softmax_weights(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"], sel,
+                                       x["kv_scale"], x["sm_scale"], r, h, rows_per_seq=2)
+            np.testing.assert_allclose(p, p_ref[h], rtol=1e-12, atol=1e-15,
+                                       err_msg=f"row {r} head {h}")
+    # the weights move with sm_scale as the definition says: a wrong scale
+    # inside the oracle would not give torch's weights at a second scale
+    p2 = oracle.softmax_weights(x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"], sel,
+                                x["kv_scale"], 3 * x["sm_scale"], 3, 2, rows_per_seq=2)
+    x3 = dict(x, sm_scale=3 * x["sm_scale"])
+    np.testing.assert_allclose(p2, torch_weights_and_rows(x3, 3, sel[3])[0][2], rtol=1e-12,
+                               atol=1e-15)
+
+
+def test_attention_error_scale_is_the_magnitude_weighted_output():
+    x = small_attend_inputs(51, L=29, top_k=12, H=3, Dl=24, ps=8, S=2, K=2)
+    rng = np.random.default_rng(4)
+    sel = np.stack([np.sort(rng.choice(int(L), 12, replace=False)) for L in x["seq_lens"]]).astype(np.int32)
+    args = (x["q"], x["kv_cache"], x["block_tables"], x["seq_lens"], sel, x["kv_scale"],
+            x["sm_scale"])
+    scale = oracle.mla_decode_abs(*args, rows_per_seq=2)
+    out = oracle.mla_decode(*args, rows_per_seq=2)
+    for r in range(4):
+        p, c = torch_weights_and_rows(x, r, sel[r])
+        np.testing.assert_allclose(scale[r], p @ np.abs(c), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(out[r], p @ c, rtol=1e-12, atol=1e-15)
+    assert (scale >= np.abs(out) - 1e-15).all()
+    # a latent whose values are all positive: the scale is the output itself
+    pos = dict(x, kv_cache=np.where(x["kv_cache"] == 0x7F, 0x7F, x["kv_cache"] & 0x7F).astype(np.uint8))
+    args_pos = (pos["q"], pos["kv_cache"], pos["block_tables"], pos["seq_lens"], sel,
+                pos["kv_scale"], pos["sm_scale"])
+    np.testing.assert_allclose(oracle.mla_decode_abs(*args_pos, rows_per_seq=2),
+                               oracle.mla_decode(*args_pos, rows_per_seq=2), rtol=1e-13)
+
+
+def test_decode_pipeline_with_several_rows_per_sequence():
+    """oracle.decode at K = 3: every row's scores, selection and attention
+    against torch computations of the three definitions on that row's own
+    sequence (r // K) and its own length."""
+    w = wl.custom(num_seqs=2, rows_per_seq=3, num_heads=4, latent_dim=32, index_heads=3,
+                  index_dim=16, top_k=20, page_size=8, seed=52, lengths="verify", base=40)
+    x = wl.make_inputs(w)
+    scores, sel, att = oracle.decode(x)
+    K = 3
+    for r in range(6):
+        s, L = r // K, int(x["seq_lens"][r])
+        qi = bf16_to_f64(x["q_idx"][r])                            # [Hi, D]
+        keys = bf16_to_f64(x["k_normed"][s, :L])                   # [L, D]
+        dots = torch.from_numpy(keys @ qi.T)                       # [L, Hi]
+        ref = (torch.relu(dots) * torch.from_numpy(x["w"][r].astype(np.float64))).sum(1).numpy()
+        np.testing.assert_allclose(scores[r][:L], ref, rtol=1e-12, atol=1e-14, err_msg=f"row {r}")
+        order = np.lexsort((np.arange(L), -ref))[:20]
+        np.testing.assert_array_equal(sel[r], np.sort(order), err_msg=f"row {r}")
+        p, c = torch_weights_and_rows(x, r, np.sort(order))
+        np.testing.assert_allclose(att[r], p @ c, rtol=1e-12, atol=1e-14, err_msg=f"row {r}")
+    # the rows of a sequence differ only by their horizon: row 2 sees two
+    # more tokens than row 0 of the same sequence
+    assert len(scores[2]) == len(scores[0]) + 2
