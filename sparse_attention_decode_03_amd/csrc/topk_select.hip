@@ -577,11 +577,17 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
     bool first = true;
     while (true) {
         shift = max(bits - kSelDigit, 0);
+        // Only keys inside the window [base, base + 2^bits) are counted: it
+        // has 2^(bits - shift) <= kSelBins bins. After a narrowing pass, keys
+        // of the bins above the old boundary bin can still fall within
+        // kSelBins units of the new base; `need` has already discounted
+        // them, so counting them again would move the cut.
+        const uint32_t nbins = 1u << (bits - shift);
 #pragma unroll
         for (int j = 0; j < N; j++) {
             if ((valid & (1u << j)) && kk[j] >= base) {
                 const uint32_t d = (kk[j] - base) >> shift;
-                if (d < (uint32_t)kSelBins)
+                if (d < nbins)
                     atomicAdd(&h[hslot(d)], 1u);
             }
         }

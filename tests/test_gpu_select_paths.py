@@ -5,16 +5,24 @@ under (score descending, index ascending) (glm5next_dsa/layer.rs source page:
 `batch_select_enabled`).
 
 Three launch shapes: rows up to 131072 tokens, rows past it (more slices
-than the others), and a top_k past 2048. In each, the rows reach every route:
-the threshold from 32-token or 4-token group keys, held in registers or
-re-read; every token a candidate; the member-list and equal-key cuts; the
-full-row fallback when candidates overflow."""
+than the others), and a top_k past 2048. The rows (tests/select_rows.py)
+reach these routes, as the CPU model of the selector confirms
+(test_select_model.py::test_gpu_route_rows_cover_every_route): rows within
+top_k; the threshold from 4-token group keys held in registers or re-read
+from memory, or from 32-token group keys, or every token a candidate; the
+finishing workgroup's candidates taken by slice or spread by an offset
+search; the exact cut in one digit pass, narrowed over several (also into
+windows under 12 bits, with more than 256 members in the boundary bin), and
+its boundary bin ranked member by member or, for one shared key, by index;
+and the full-row fallback when the candidates overflow it."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from sparse_attention_decode_03_amd import dsa
+
+from select_rows import crafted_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -23,47 +31,6 @@ ROUTES = {
     "135168 tokens": (135168, 2048),
     "top_k 2304": (131072, 2304),
 }
-
-
-def crafted_rows(max_len, top_k):
-    rng = np.random.default_rng(2024)
-    rows = []
-
-    def add(name, L, values):
-        L = min(L, max_len)
-        full = np.zeros(max_len, np.float32)
-        full[:L] = values[:L]
-        rows.append((name, L, full))
-
-    n = max_len
-    add("normal, full length", n, rng.standard_normal(n).astype(np.float32))
-    add("normal, 40000 tokens", 40000, rng.standard_normal(n).astype(np.float32))
-    add("normal, 30000 tokens", 30000, rng.standard_normal(n).astype(np.float32))
-    add("all equal, overflow to the full-row path", 20000, np.ones(n, np.float32))
-    add("seven integer levels, overflow", n, rng.integers(-3, 4, n).astype(np.float32))
-    add("ascending ramp", n, np.arange(n, dtype=np.float32))
-    add("descending ramp", 100000, -np.arange(n, dtype=np.float32))
-    add("student-t tails", n, rng.standard_t(3, n).astype(np.float32))
-    add("every token a candidate", 4 * top_k - 5, rng.standard_normal(n).astype(np.float32))
-    add("exactly top_k 4-token groups", 4 * top_k - 1, rng.standard_normal(n).astype(np.float32))
-    add("one past top_k", top_k + 1, rng.standard_normal(n).astype(np.float32))
-    zeros = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0))
-    zeros[rng.choice(70000, 100, replace=False)] = rng.random(100).astype(np.float32) + 0.5
-    add("signed zeros with a few positives", 70000, zeros)
-    add("ties at the threshold (one decimal)", n,
-        np.round(rng.standard_normal(n), 1).astype(np.float32))
-    add("negative scores only", 50000, -np.abs(rng.standard_normal(n)).astype(np.float32))
-    # a tight cluster (keys within ~800 units) between two far outliers: the
-    # first threshold digit is coarse, so it is narrowed over several digits
-    cluster = (1.0 + 1e-4 * rng.random(n)).astype(np.float32)
-    cluster[rng.integers(0, n)] = np.float32(1e30)
-    cluster[rng.integers(0, n)] = np.float32(-1e30)
-    add("clustered keys between far outliers", n, cluster)
-    # top-k packed into the row's last few thousand tokens
-    late = rng.standard_normal(n).astype(np.float32)
-    late[-3000:] += 50.0
-    add("winners packed at the end", n, late)
-    return rows
 
 
 @pytest.mark.parametrize("route", list(ROUTES))
