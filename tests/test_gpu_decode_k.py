@@ -80,3 +80,13 @@ def test_verify_rows_bit_identical_when_rows_select_everything():
     inputs = small(num_seqs=2, rows_per_seq=4, lengths="verify", base=2046, top_k=2048,
                    seed=110, page_size=16)
     assert_serial_equals_batched(inputs)
+
+
+def test_verify_workload_at_full_size_is_bit_identical_to_serial_calls():
+    """The K-token verify workload itself (16 sequences x 4 rows, L = 16385
+    .. 16388): its one call scores with the four-row index pass and attends
+    in 64-head workgroups over 512 workgroups, while each serial call (16
+    rows) runs the one-row index pass and smaller head groups; the bytes
+    must agree."""
+    inputs = wl.make_inputs(wl.WORKLOADS["kverify"])
+    assert_serial_equals_batched(inputs)

@@ -1,22 +1,31 @@
-"""The four benchmark workloads at their full sizes, through dsa_decode_k in the
-launch configuration the benchmark times, checked row by row against the CPU
-oracle: scores within tolerance, selection exact on the GPU's own scores,
-attention within tolerance over the GPU's own selection."""
+"""The five workloads at their full sizes, through dsa_decode_k in the launch
+configuration the benchmark times, checked row by row against the CPU
+oracle: scores within tolerance; selection exact on the GPU's own scores and,
+end to end, equal to the oracle's own selection on its fp64 scores except for
+tokens within 1e-6 relative of a row's cut; attention within the 2e-2
+contract and the bound derived from the kernel's roundings, over the GPU's
+own selection. Each case prints its largest errors."""
 import pytest
 
 from sparse_attention_decode_03_amd import workloads as wl
 
-from gpu_common import check_attention, check_scores, check_selection, host, run_step
+from gpu_common import (check_attention, check_scores, check_selection,
+                        check_selection_end_to_end, host, run_step)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["single", "batched", "kverify", "long"])
+@pytest.mark.parametrize("name", ["tiny", "single", "batched", "kverify", "long"])
 def test_full_size_workload(name):
     inputs = wl.make_inputs(wl.WORKLOADS[name])
+    print(f"workload {name}: {len(inputs['seq_lens'])} rows", flush=True)
     step = run_step(inputs)
     scores, sel, out = host(step)
     rows = range(inputs["seq_lens"].shape[0])
-    check_scores(inputs, scores, rows)
+    refs, score_worst = check_scores(inputs, scores, rows)
     check_selection(inputs, scores, sel, rows)
-    check_attention(inputs, sel, out, rows)
+    differ = check_selection_end_to_end(inputs, refs, sel, rows)
+    att_abs, att_rel = check_attention(inputs, sel, out, rows)
+    print(f"workload {name}: score error up to {score_worst:.3g} of its tolerance; "
+          f"{differ} rows select differently from the fp64 oracle; attention error up to "
+          f"{att_abs:.3g} absolute, {att_rel:.3g} of the derived bound", flush=True)

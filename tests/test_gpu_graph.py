@@ -3,16 +3,19 @@ contract of the boundary: no allocation, no memset, no host round trip inside
 a call; grids sized from max_len, lengths read on the device). One capture is
 replayed at two sets of lengths -- shorter rows, then rows grown in place up
 to max_len -- with eager work and synchronisations between replays, and every
-replay must equal the eager call at the same lengths byte for byte
-(glm5next_dsa/layer.rs source page: the graph-safe ceiling launch and the
-removal of host-to-device copies from `decode_k`)."""
+replay must equal the eager call at the same lengths byte for byte and agree
+with the CPU oracle at those lengths (glm5next_dsa/layer.rs source page: the
+graph-safe ceiling launch and the removal of host-to-device copies from
+`decode_k`; its note that a ceiling baked in at capture made long replays
+diverge)."""
 import numpy as np
 import pytest
 import torch
 
 from sparse_attention_decode_03_amd import dsa
 
-from gpu_common import small
+from gpu_common import (bf16_codes_to_f64, check_attention, check_scores, check_selection,
+                        check_selection_end_to_end, small)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +70,13 @@ def test_captured_step_replays_like_eager_at_any_length():
         torch.cuda.synchronize()
         got = snapshot(step, lens)
         assert_same(got, ref_short if lens is short_lens else ref_long, f"replay {i}")
+        # and the replayed step against the oracle at these lengths
+        at = dict(inputs, seq_lens=lens)
+        rows = range(len(lens))
+        scores = step.scores.cpu().numpy()
+        sel = step.sel.cpu().numpy()
+        out = bf16_codes_to_f64(step.out.cpu().numpy().view(np.uint16))
+        refs, _ = check_scores(at, scores, rows)
+        check_selection(at, scores, sel, rows)
+        check_selection_end_to_end(at, refs, sel, rows)
+        check_attention(at, sel, out, rows)

@@ -9,8 +9,8 @@ import oracle
 from sparse_attention_decode_03_amd import dsa
 from sparse_attention_decode_03_amd import workloads as wl
 
-from gpu_common import (ATT_ATOL, check_attention, check_scores, check_selection, host, run_step,
-                        small, bf16_codes_to_f64)
+from gpu_common import (assert_attention_row, check_attention, check_scores, check_selection,
+                        check_selection_end_to_end, host, run_step, small, bf16_codes_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,8 +19,9 @@ def full_check(inputs, rows=None):
     step = run_step(inputs)
     scores, sel, out = host(step)
     rows = range(inputs["seq_lens"].shape[0]) if rows is None else rows
-    check_scores(inputs, scores, rows)
+    refs, _ = check_scores(inputs, scores, rows)
     check_selection(inputs, scores, sel, rows)
+    check_selection_end_to_end(inputs, refs, sel, rows)
     check_attention(inputs, sel, out, rows)
     return step, scores, sel, out
 
@@ -213,11 +214,7 @@ def test_stage_entry_points_match_the_fused_step(case):
     for r in range(len(lens)):
         ids = sel[r, :min(int(lens[r]), inputs["top_k"])]
         keep = ids[bt[r // K, ids // ps] >= 0].astype(np.int32)
-        ref = oracle.mla_decode(inputs["q"][r:r + 1], inputs["kv_cache"], bt[r // K:r // K + 1],
-                                lens[r:r + 1], keep[None], inputs["kv_scale"], inputs["sm_scale"],
-                                1)[0]
-        err = np.abs(out[r] - ref).max()
-        assert err <= ATT_ATOL, f"row {r}: max abs error {err:.3g}"
+        assert_attention_row(inputs, r, keep, out[r])
 
 
 def test_empty_rows_and_out_of_contract_ids_are_safe():
@@ -237,8 +234,67 @@ def test_empty_rows_and_out_of_contract_ids_are_safe():
     torch.cuda.synchronize()
     got = bf16_codes_to_f64(step.out.cpu().numpy().view(np.uint16))[1]
     keep = sel.cpu().numpy()[1, 2:]
-    ref = oracle.mla_decode(inputs["q"][1:2], inputs["kv_cache"], inputs["block_tables"][1:2],
-                            np.array([600], np.int32), keep[None].astype(np.int32),
-                            inputs["kv_scale"], inputs["sm_scale"], 1)[0]
     # the reference attends over the 254 valid ids that remain
-    assert np.abs(got - ref).max() <= 2e-2
+    assert_attention_row(inputs, 1, keep, got)
+
+
+@pytest.mark.parametrize("rows", [6, 40])
+def test_dominant_token_at_chunk_boundaries(rows):
+    """One selected token carries about half of every head's softmax mass,
+    placed at slot 0, 255, 256, 1023, 1024 or 2047 of a 2048-slot selection
+    (8 chunks of 256 slots): the chunk edges and the row's end. A slot lost
+    or counted twice at a chunk edge moves the output by ~0.2 per element,
+    ten times the contract's 2e-2. Six rows run 16-head workgroups, forty
+    rows 64-head ones (the kernel picks the group from the batch)."""
+    L, top_k = 4096, 2048
+    inputs = small(num_seqs=rows, rows_per_seq=1, context=L, top_k=top_k, seed=140 + rows)
+    rng = np.random.default_rng(140 + rows)
+    slots = [0, 255, 256, 1023, 1024, 2047]
+    H, ps, kv_scale = inputs["num_heads"], inputs["page_size"], inputs["kv_scale"]
+    sel = np.stack([np.sort(rng.choice(L, top_k, replace=False)) for _ in range(rows)]).astype(np.int32)
+    # every head's query is N(s, 1) for one sign pattern s; the dominant
+    # token's dequantised latent row is 0.375 * s (the E4M3 code of 0.75
+    # times kv_scale 0.5, exact), so its logit is about 0.375 * 512 /
+    # sqrt(512) = 8.5, while the other 2047 logits are ~N(0, 2) and their
+    # exponentials sum to about 2047 e = e^8.6
+    for r in range(rows):
+        sgn = rng.choice([-1.0, 1.0], 512).astype(np.float32)
+        qf = rng.standard_normal((H, 512)).astype(np.float32) + sgn
+        inputs["q"][r] = wl.f32_to_bf16_codes(qf)
+        t = int(sel[r, slots[r % len(slots)]])
+        page = inputs["block_tables"][r, t // ps]
+        inputs["kv_cache"][page, t % ps] = wl.f32_to_e4m3_codes(0.375 * sgn / kv_scale)
+    step = dsa.DeviceStep(inputs)
+    d_sel = torch.from_numpy(sel).cuda()
+    dsa.mla_decode(step.shape, step.q, step.kv_cache, step.block_tables, step.seq_lens, d_sel,
+                   step.kv_scale, step.sm_scale, step.out, step.ws)
+    torch.cuda.synchronize()
+    out = bf16_codes_to_f64(step.out.cpu().numpy().view(np.uint16))
+    for r in range(rows):
+        assert_attention_row(inputs, r, sel[r], out[r])
+        # power: without the dominant token the oracle's output is far away
+        j = slots[r % len(slots)]
+        drop = np.delete(sel[r], j)
+        ref_drop = oracle.mla_decode(inputs["q"][r:r + 1], inputs["kv_cache"],
+                                     inputs["block_tables"][r:r + 1], inputs["seq_lens"][r:r + 1],
+                                     drop[None], inputs["kv_scale"], inputs["sm_scale"], 1)[0]
+        assert np.abs(out[r] - ref_drop).max() > 0.1, f"row {r}: slot {j} carries too little mass"
+
+
+def test_check_metadata_on_device_arrays():
+    """dsa_check_metadata reads the device arrays in stream order: a step's own
+    lengths, block table and selection pass; a selected id past its row's
+    length and an unmapped reachable page are named."""
+    inputs = small(num_seqs=2, rows_per_seq=2, lengths="verify", base=3000, top_k=512, seed=150)
+    step = run_step(inputs)
+    dsa.check_metadata(step.shape, step.seq_lens, step.block_tables, step.sel)
+    bad_sel = step.sel.clone()
+    bad_sel[3, 7] = int(inputs["seq_lens"][3])
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.check_metadata(step.shape, step.seq_lens, step.block_tables, bad_sel)
+    assert e.value.code == dsa.DSA_EMETADATA and "sel[3][7]" in e.value.message
+    bad_bt = step.block_tables.clone()
+    bad_bt[1, 5] = inputs["num_pages"]
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.check_metadata(step.shape, step.seq_lens, bad_bt, step.sel)
+    assert "block_tables[1][5]" in e.value.message
