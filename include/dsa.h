@@ -62,6 +62,11 @@ extern "C" {
 #define DSA_ERANGE (-3)       /* sizes that do not fit one another                */
 #define DSA_EWORKSPACE (-4)   /* workspace null or smaller than dsa_workspace_bytes */
 #define DSA_ELAUNCH (-5)      /* the HIP runtime refused a launch                 */
+#define DSA_EMETADATA (-6)    /* dsa_check_metadata found out-of-contract values  */
+
+/* `where` argument of dsa_check_metadata */
+#define DSA_META_DEVICE 0     /* the arrays are device memory                     */
+#define DSA_META_HOST 1       /* the arrays are host memory                       */
 
 /*
  * Problem shape. Names follow the layer's config (layer.rs: the
@@ -255,6 +260,32 @@ size_t dsa_score_stride(const dsa_shape *shape);
  * `bt_entries_needed` and its bt_trim_tests module). Host-only helper.
  */
 size_t dsa_bt_entries_needed(size_t seq_len, size_t k, size_t block_size);
+
+/*
+ * Check of the device-resident metadata that the step entry points read
+ * without checking it (they cannot without a synchronisation): a test and
+ * debugging aid, never on the timed path. It is the counterpart of the
+ * pages' refusals before any launch (layer.rs `decode_k`: the row-count and
+ * metadata checks that bail out before touching the device, and the refusal
+ * of a block-table row too short for the positions it must cover).
+ * Checks, for the rows and sequences of `shape`:
+ *   - 0 <= seq_lens[r] <= max_len;
+ *   - every block-table entry a row can reach, block_tables[s][b] for
+ *     b < ceil(max_j L_{s,j} / page_size), lies in [0, num_pages);
+ *   - if sel is not NULL: the first n_r = min(top_k, L_r) ids of sel[r] lie
+ *     in [0, L_r) and are distinct (a selection is a set), and every slot
+ *     past n_r holds -1 (the padding dsa_topk_select writes).
+ * where = DSA_META_DEVICE: the arrays are device memory; they are copied to
+ * the host in the order of `stream` (so they reflect the work enqueued
+ * before), which this call then synchronises. where = DSA_META_HOST: the
+ * arrays are host memory and nothing touches the device. Unlike the step
+ * entry points this call synchronises and allocates host memory.
+ * Returns DSA_OK, a refusal code for bad arguments, or DSA_EMETADATA with
+ * dsa_last_error() naming the first violation and the number found.
+ */
+int dsa_check_metadata(const dsa_shape *shape, const int32_t *seq_lens,
+                       const int32_t *block_tables, const int32_t *sel, int where,
+                       void *stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *dsa_last_error(void);

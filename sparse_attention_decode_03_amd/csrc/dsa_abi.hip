@@ -7,6 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "dsa.h"
 #include "dsa_kernels.h"
 
@@ -365,6 +368,87 @@ int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent
                                             kv_scale, kv_cache, (uint16_t *)k_normed,
                                             (hipStream_t)stream),
                     "cache_write");
+}
+
+int dsa_check_metadata(const dsa_shape *shape, const int32_t *seq_lens,
+                       const int32_t *block_tables, const int32_t *sel, int where, void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    if (!seq_lens || !block_tables)
+        return fail(DSA_EINVAL, "seq_lens and block_tables must not be NULL");
+    if (where != DSA_META_DEVICE && where != DSA_META_HOST)
+        return fail(DSA_EINVAL, "where %d is neither DSA_META_DEVICE nor DSA_META_HOST", where);
+    const int R = ls.num_rows, S = ls.num_seqs, K = ls.rows_per_seq;
+    const size_t n_bt = (size_t)S * ls.max_blocks;
+    const size_t n_sel = sel ? (size_t)R * ls.top_k : 0;
+    std::vector<int32_t> h_len, h_bt, h_sel;
+    const int32_t *len = seq_lens, *bt = block_tables, *sl = sel;
+    if (where == DSA_META_DEVICE) {
+        hipStream_t st = (hipStream_t)stream;
+        h_len.resize(R);
+        h_bt.resize(n_bt);
+        h_sel.resize(n_sel);
+        if (hipMemcpyAsync(h_len.data(), seq_lens, R * sizeof(int32_t), hipMemcpyDeviceToHost,
+                           st) != hipSuccess ||
+            hipMemcpyAsync(h_bt.data(), block_tables, n_bt * sizeof(int32_t),
+                           hipMemcpyDeviceToHost, st) != hipSuccess ||
+            (sel && hipMemcpyAsync(h_sel.data(), sel, n_sel * sizeof(int32_t),
+                                   hipMemcpyDeviceToHost, st) != hipSuccess) ||
+            hipStreamSynchronize(st) != hipSuccess)
+            return fail(DSA_ELAUNCH, "copying the metadata to the host failed: %s",
+                        hipGetErrorString(hipGetLastError()));
+        len = h_len.data();
+        bt = h_bt.data();
+        sl = sel ? h_sel.data() : nullptr;
+    }
+    long long bad = 0;
+    char first[256] = "";
+    auto note = [&](const char *fmt, auto... args) {
+        if (bad++ == 0)
+            snprintf(first, sizeof first, fmt, args...);
+    };
+    for (int r = 0; r < R; r++)
+        if (len[r] < 0 || len[r] > ls.max_len)
+            note("seq_lens[%d] = %d outside [0, max_len = %d]", r, len[r], ls.max_len);
+    for (int s = 0; s < S; s++) {
+        int lmax = 0;
+        for (int j = 0; j < K; j++)
+            lmax = std::max(lmax, std::min(std::max(len[s * K + j], 0), ls.max_len));
+        const int nb = (lmax + ls.page_size - 1) / ls.page_size; // <= max_blocks
+        for (int b = 0; b < nb; b++) {
+            const int32_t p = bt[(size_t)s * ls.max_blocks + b];
+            if (p < 0 || p >= ls.num_pages)
+                note("block_tables[%d][%d] = %d outside [0, num_pages = %d] (sequence %d reaches "
+                     "%d blocks)", s, b, p, ls.num_pages, s, nb);
+        }
+    }
+    if (sl) {
+        std::vector<int32_t> ids;
+        for (int r = 0; r < R; r++) {
+            const int L = std::min(std::max(len[r], 0), ls.max_len);
+            const int n = std::min(ls.top_k, L);
+            const int32_t *row = sl + (size_t)r * ls.top_k;
+            ids.assign(row, row + n);
+            for (int j = 0; j < n; j++)
+                if (row[j] < 0 || row[j] >= L)
+                    note("sel[%d][%d] = %d outside [0, L_r = %d)", r, j, row[j], L);
+            std::sort(ids.begin(), ids.end());
+            for (int j = 1; j < n; j++)
+                if (ids[j] == ids[j - 1])
+                    note("sel[%d] holds id %d more than once", r, ids[j]);
+            for (int j = n; j < ls.top_k; j++)
+                if (row[j] != -1)
+                    note("sel[%d][%d] = %d past n_r = %d (padding must be -1)", r, j, row[j], n);
+        }
+    }
+    if (bad)
+        return fail(DSA_EMETADATA, "%lld out-of-contract value%s; first: %s", bad,
+                    bad == 1 ? "" : "s", first);
+    return DSA_OK;
 }
 
 } // extern "C"

@@ -21,6 +21,9 @@ DSA_EUNSUPPORTED = -2
 DSA_ERANGE = -3
 DSA_EWORKSPACE = -4
 DSA_ELAUNCH = -5
+DSA_EMETADATA = -6
+DSA_META_DEVICE = 0
+DSA_META_HOST = 1
 
 # Every symbol include/dsa.h declares.
 EXPORTS = (
@@ -35,6 +38,7 @@ EXPORTS = (
     "dsa_pool_score_stride",
     "dsa_score_stride",
     "dsa_bt_entries_needed",
+    "dsa_check_metadata",
     "dsa_last_error",
 )
 
@@ -120,6 +124,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_topk_select_pooled.restype = i32
     lib.dsa_bt_entries_needed.argtypes = [sz, sz, sz]
     lib.dsa_bt_entries_needed.restype = sz
+    lib.dsa_check_metadata.argtypes = [S, P, P, P, i32, P]
+    lib.dsa_check_metadata.restype = i32
     lib.dsa_last_error.argtypes = []
     lib.dsa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -211,6 +217,22 @@ def decode_k(shape: Shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_le
                                _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), kv_scale,
                                sm_scale, _ptr(scores), _ptr(sel), _ptr(out), _ptr(ws), nb,
                                _stream(stream)))
+
+
+def check_metadata(shape: Shape, seq_lens, block_tables, sel=None, stream=None) -> None:
+    """Raises DsaError (DSA_EMETADATA) if the lengths, the reachable
+    block-table entries or the selection are out of contract. Torch CUDA
+    tensors are checked in stream order (a synchronising call); numpy arrays
+    are checked on the host."""
+    import numpy as np
+    if isinstance(seq_lens, np.ndarray):
+        arrs = [np.ascontiguousarray(a, dtype=np.int32) if a is not None else None
+                for a in (seq_lens, block_tables, sel)]
+        ptrs = [a.ctypes.data if a is not None else None for a in arrs]
+        _check(load().dsa_check_metadata(ctypes.byref(shape), *ptrs, DSA_META_HOST, None))
+        return
+    _check(load().dsa_check_metadata(ctypes.byref(shape), _ptr(seq_lens), _ptr(block_tables),
+                                     _ptr(sel), DSA_META_DEVICE, _stream(stream)))
 
 
 def cache_write(shape: Shape, kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables,

@@ -85,8 +85,10 @@ def test_pointer_and_workspace_refusals():
 
 
 def test_bt_entries_needed_matches_the_pages_trim_tests():
-    # literals of the bt_trim_tests module on the glm5next_dsa/layer.rs page
-    assert 262_144 // 16 + 2 == 16_386
+    # literals of the bt_trim_tests module on the glm5next_dsa/layer.rs page:
+    # the pool a whole 262,144-token context claims is 16,386 entries, past
+    # the 16,384-entry buffer; a 20-token sequence verifying 3 needs 3
+    assert dsa.bt_entries_needed(262_144, 0, 16) == 16_386
     assert dsa.bt_entries_needed(20, 3, 16) == 3
     assert dsa.bt_entries_needed(8, 1, 0) == 11
     assert dsa.bt_entries_needed(16_384, 4, 16) <= 16_384
@@ -107,3 +109,55 @@ def test_pooled_helpers_size_by_pools_and_refuse_bad_pool_sizes():
     assert dsa.pooled_workspace_bytes(sh, 1025) == 0
     # a pool longer than every row still has a layout (rows keep their tails)
     assert dsa.pooled_workspace_bytes(good_shape(max_len=100, k_capacity=100), 512) > 0
+
+
+# ---------------------------------------------------------------------------
+# dsa_check_metadata on host arrays (through the C ABI; no device touched)
+
+def meta_case():
+    import numpy as np
+    sh = dsa.Shape(num_seqs=2, rows_per_seq=2, num_heads=8, latent_dim=512, index_heads=4,
+                   index_dim=64, top_k=4, page_size=4, max_len=10, k_capacity=10,
+                   max_blocks_per_seq=3, num_pages=6)
+    lens = np.array([9, 10, 3, 4], np.int32)
+    bt = np.array([[5, 0, 2], [4, -1, -1]], np.int32)     # sequence 1 reaches one page
+    sel = np.array([[0, 3, 7, 8], [1, 2, 5, 9], [0, 1, 2, -1], [0, 1, 2, 3]], np.int32)
+    return sh, lens, bt, sel
+
+
+def test_check_metadata_accepts_in_contract_metadata():
+    sh, lens, bt, sel = meta_case()
+    dsa.check_metadata(sh, lens, bt, sel)
+    dsa.check_metadata(sh, lens, bt)          # without a selection
+
+
+@pytest.mark.parametrize("what,edit,needle", [
+    ("length past max_len", lambda l, b, s: l.__setitem__(1, 11), "seq_lens[1] = 11"),
+    ("negative length", lambda l, b, s: l.__setitem__(2, -1), "seq_lens[2] = -1"),
+    ("reachable page unmapped", lambda l, b, s: b.__setitem__((0, 2), -1), "block_tables[0][2] = -1"),
+    ("reachable page past the pool", lambda l, b, s: b.__setitem__((1, 0), 6), "block_tables[1][0] = 6"),
+    ("id past the row's length", lambda l, b, s: s.__setitem__((2, 2), 3), "sel[2][2] = 3"),
+    ("negative id", lambda l, b, s: s.__setitem__((0, 0), -1), "sel[0][0] = -1"),
+    ("id twice", lambda l, b, s: s.__setitem__((3, 3), 2), "more than once"),
+    ("padding not -1", lambda l, b, s: s.__setitem__((2, 3), 0), "padding"),
+])
+def test_check_metadata_names_the_first_violation(what, edit, needle):
+    sh, lens, bt, sel = meta_case()
+    edit(lens, bt, sel)
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.check_metadata(sh, lens, bt, sel)
+    assert e.value.code == dsa.DSA_EMETADATA, what
+    assert needle in e.value.message, (what, e.value.message)
+
+
+def test_check_metadata_ignores_unreachable_entries_and_counts_violations():
+    sh, lens, bt, sel = meta_case()
+    bt[1, 1:] = 99                 # past the pages sequence 1 reaches: never read
+    dsa.check_metadata(sh, lens, bt, sel)
+    bt[0, :] = 99                  # three reachable entries out of the pool
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.check_metadata(sh, lens, bt, sel)
+    assert e.value.message.startswith("3 out-of-contract values")
+    lib = dsa.load()
+    assert lib.dsa_check_metadata(ctypes.byref(sh), None, 4096, None, 1, None) == dsa.DSA_EINVAL
+    assert lib.dsa_check_metadata(ctypes.byref(sh), 4096, 4096, None, 7, None) == dsa.DSA_EINVAL
