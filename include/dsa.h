@@ -191,6 +191,27 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w,
                  size_t ws_bytes, void *stream);
 
 /*
+ * dsa_decode_k for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same kernels and results as dsa_decode_k (byte for byte), with the
+ * workspace taken from an array the library holds on each device instead of
+ * from the caller: DSA_NOALLOC_SCRATCH_BYTES bytes per device, claimed when
+ * the library's code first loads on that device and kept until the process
+ * ends. The call allocates nothing. A shape whose dsa_workspace_bytes exceeds
+ * the array is refused with DSA_EWORKSPACE before anything is enqueued. All
+ * calls on one device share its array, so calls that may overlap on one
+ * device (other streams, other threads) race and must be serialised by the
+ * caller; the array needs no clearing between calls (each call writes every
+ * part it reads). The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) with that device current.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int dsa_decode_k_noalloc(const dsa_shape *shape, const void *q_idx, const float *w,
+                         const void *k_normed, const void *q, const uint8_t *kv_cache,
+                         const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
+                         float sm_scale, float *scores, int32_t *sel, void *out, void *stream);
+
+/*
  * Pooled selection (the selector of the pages' own layer, on pools of kp
  * consecutive tokens) and its expansion back to token ids. layer.rs, doc of
  * the prefill row-group selector: a pool is a candidate of row r only when it

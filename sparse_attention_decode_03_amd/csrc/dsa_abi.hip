@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "dsa.h"
@@ -176,6 +177,40 @@ Workspace workspace_layout(const LaunchShape &ls)
 
 } // namespace dsa
 
+namespace {
+
+// Library-owned workspace of dsa_decode_k_noalloc: one per device, held until
+// the process ends. Host code never passes `scratch` itself to a kernel or a
+// copy (on the host the name is a stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current). Returns DSA_OK or a refusal.
+int scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(DSA_ELAUNCH, "no usable current device (hipGetDevice gave %d)", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(DSA_ELAUNCH, "hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                        dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
+
+} // namespace
+
 extern "C" {
 
 size_t dsa_workspace_bytes(const dsa_shape *shape)
@@ -340,6 +375,31 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, cons
                        "mla_decode")))
         return rc;
     return DSA_OK;
+}
+
+int dsa_decode_k_noalloc(const dsa_shape *shape, const void *q_idx, const float *w,
+                         const void *k_normed, const void *q, const uint8_t *kv_cache,
+                         const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
+                         float sm_scale, float *scores, int32_t *sel, void *out, void *stream)
+{
+    g_err[0] = 0;
+    dsa::LaunchShape ls;
+    int rc;
+    if ((rc = check_shape(shape, &ls)) != DSA_OK)
+        return rc;
+    const size_t need = dsa::workspace_layout(ls).total;
+    if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+        return fail(DSA_EWORKSPACE,
+                    "this shape needs %zu bytes of workspace, above the %zu-byte scratch array of "
+                    "dsa_decode_k_noalloc (use dsa_decode_k with a caller workspace)",
+                    need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws)) != DSA_OK)
+        return rc;
+    // every part of the workspace is written before it is read within a call,
+    // so the contents a previous call left need no clearing
+    return dsa_decode_k(shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_lens, kv_scale,
+                        sm_scale, scores, sel, out, ws, (size_t)DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent_w,

@@ -24,6 +24,7 @@ DSA_ELAUNCH = -5
 DSA_EMETADATA = -6
 DSA_META_DEVICE = 0
 DSA_META_HOST = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/dsa.h declares.
 EXPORTS = (
@@ -32,6 +33,7 @@ EXPORTS = (
     "dsa_topk_select",
     "dsa_mla_decode",
     "dsa_decode_k",
+    "dsa_decode_k_noalloc",
     "dsa_cache_write",
     "dsa_topk_select_pooled",
     "dsa_pooled_workspace_bytes",
@@ -112,6 +114,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_mla_decode.restype = i32
     lib.dsa_decode_k.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P, sz, P]
     lib.dsa_decode_k.restype = i32
+    lib.dsa_decode_k_noalloc.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P]
+    lib.dsa_decode_k_noalloc.restype = i32
     lib.dsa_cache_write.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P]
     lib.dsa_cache_write.restype = i32
     lib.dsa_score_stride.argtypes = [S]
@@ -233,6 +237,15 @@ def check_metadata(shape: Shape, seq_lens, block_tables, sel=None, stream=None) 
         return
     _check(load().dsa_check_metadata(ctypes.byref(shape), _ptr(seq_lens), _ptr(block_tables),
                                      _ptr(sel), DSA_META_DEVICE, _stream(stream)))
+
+
+def decode_k_noalloc(shape: Shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_lens,
+                     kv_scale: float, sm_scale: float, scores, sel, out, stream=None) -> None:
+    """dsa_decode_k with the library's per-device scratch array as workspace."""
+    _check(load().dsa_decode_k_noalloc(ctypes.byref(shape), _ptr(q_idx), _ptr(w), _ptr(k_normed),
+                                       _ptr(q), _ptr(kv_cache), _ptr(block_tables),
+                                       _ptr(seq_lens), kv_scale, sm_scale, _ptr(scores),
+                                       _ptr(sel), _ptr(out), _stream(stream)))
 
 
 def cache_write(shape: Shape, kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables,
