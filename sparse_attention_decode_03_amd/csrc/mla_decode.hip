@@ -8,27 +8,34 @@
 //
 // Decomposition (a function of the row alone, never of R, so every row is
 // bit-reproducible whichever rows share a launch):
-//  - A row's selection is cut into chunks of kAttChunk slots. One workgroup
-//    of 8 waves covers one chunk for a group of G heads (16, 32 or 64), in
-//    steps of 32 tokens. Each token's 512-byte FP8 row is gathered through
-//    the block table with
-//    coalesced 16-byte loads, dequantised exactly to bf16 (E4M3 is a subset
-//    of bf16; kv_scale is folded into the logit scale and the output) and
-//    parked token-major in one of three LDS tiles, in padded rows that keep
-//    the operand reads below free of bank conflicts.
-//  - Two roles, one barrier per step. Waves 0-3 score: wave w holds the
-//    query of heads 16w..16w+15 in registers and computes S^T[token, head]
-//    on 16x16x32 bf16 MFMA (the tile as A, the query as B), then the online
-//    softmax in fp32 (log2 domain, exp2, fixed-order reductions, lazy
-//    rescale); the bf16 probabilities go to a small LDS buffer in the PV
-//    operand's k order. Waves 4-7 accumulate: wave v holds O[G heads,
-//    latent columns 128v..128v+127] and runs PV on 16x16x32 bf16 MFMA (P as
-//    A, the tile as B through LDS transpose loads, ds_read_tr16_b64); they
-//    also dequantise and stage the tiles and keep the gathers in flight.
-//    While the scoring waves work on step i + 1, the accumulating waves run
-//    PV of step i and stage step i + 2, so the matrix cores of every SIMD
-//    see both products at once. Each result element is still produced by
-//    the same operations in the same order, step after step.
+//  - A row's selection is cut into chunks of kAttChunk (256) slots, eight
+//    steps of 32 tokens. One workgroup of 8 waves covers one chunk for a
+//    group of G heads (16, 32 or 64), in four phases, every wave in each:
+//  1. Gather: wave w resolves step w's 32 slots through the block table and
+//     copies their FP8 latent rows (512 bytes each) from HBM straight into
+//     its LDS step tile with the gfx950 LDS-direct loads
+//     (global_load_lds_dwordx4: 16 bytes per lane, no registers). Rows are
+//     token-major in a tile, their 16-byte chunks XOR-swizzled by the row
+//     index, so the operand reads below touch every LDS bank evenly. One
+//     barrier publishes all eight tiles.
+//  2. QK: S^T[token, head] = tile (16 tokens x latent) x q^T on 16x16x32
+//     bf16 MFMA, one chain of 16 k-steps per (16-token tile, 16-head tile);
+//     the FP8 operand is converted to bf16 in registers (exact: every E4M3
+//     value is a bf16 value; kv_scale is folded into the logit scale and the
+//     output). Each wave owns one head tile and 2, 4 or 8 of the 16 token
+//     tiles; the per-head maxima of the chunk meet through LDS.
+//  3. Softmax over the chunk, in fp32 and exact: m the chunk's largest
+//     logit (log2 domain), p = exp2(z - m) rounded to bf16 for PV, and
+//     l = the 16 token-tile sums added in tile order (each tile sum in a
+//     fixed lane order). P goes to LDS in the PV operand's k order, 32 heads
+//     at a time.
+//  4. PV, transposed: O^T[latent col, head] += V^T P^T, the tile as A through
+//     the gfx950 8-bit transpose reads (ds_read_b64_tr_b8: a 16-lane group
+//     receives 8 token rows of one 16-column block) converted to bf16, P as
+//     B; wave w holds latent columns 64 w .. 64 w + 63 of every head, one
+//     MFMA chain over the eight steps per (16-column tile, 16-head tile).
+//  Every sum above has one order whatever G, so a head's output is the same
+//  bits whichever heads share its workgroup.
 //  - A row with one chunk writes its bf16 output directly. Otherwise every
 //    chunk writes (m, l) in fp32 and its unnormalised O rounded to bf16 (the
 //    precision of the output; half the partial traffic), and k_mla_merge
@@ -39,60 +46,72 @@
 
 namespace dsa {
 
-constexpr int kAttThreads = 512;  // 8 waves, two per SIMD: one scoring, one accumulating
-constexpr int kStep = 32;            // tokens per LDS tile
-constexpr int kTiles = 3;            // tiles in LDS: scored, accumulated, being staged
-constexpr int kLat = 512;            // latent width
-constexpr int kRowChunks = kLat / 8; // 16-byte chunks per bf16 latent row (64)
-constexpr int kPvCols = kLat / 4;    // latent columns of one accumulating wave (128)
-constexpr int kPvTiles = kPvCols / 16; // its 16-column MFMA tiles (8)
-constexpr int kMaxSteps = kAttChunk / kStep;
-// LDS tile rows (a token's bf16 latent) are padded from 1024 to 1056 bytes
-// (66 chunks): measured on gfx950 the fastest stride for the QK operand
-// reads (16 rows at one 16-byte column per lane group), and within 10 % of
-// the best for the PV transpose reads. Addresses stay a lane base plus
-// compile-time offsets.
-constexpr int kRowStride = kRowChunks + 2; // in 16-byte chunks
-// Probability rows (one head, 32 bf16) are padded from 64 to 80 bytes: 16
-// consecutive heads read at one 16-byte column hit 16 distinct 4-bank groups.
-constexpr int kPRowBytes = 80;
+constexpr int kAttThreads = 512;  // 8 waves, two per SIMD
+constexpr int kAttWaves = kAttThreads / kWave;
+constexpr int kStep = 32;         // tokens per step tile
+constexpr int kLat = 512;         // latent width (bytes of an FP8 row)
+constexpr int kMaxSteps = kAttChunk / kStep;     // 8 (one per wave)
+constexpr int kTokTiles = kAttChunk / 16;        // 16-token MFMA tiles of a chunk
+constexpr int kTileBytes = kStep * kLat;         // 16 KiB of FP8 per step
+constexpr int kDmaPerStep = kTileBytes / (kWave * 16); // LDS-direct loads per step tile (16)
+constexpr int kPvColTiles = kLat / 16 / kAttWaves;     // 16-column tiles per wave (4)
+// P in LDS: every head of the group for as many tokens as fit beside the
+// ring (256 with 16 or 32 heads, 128 with 64: then PV runs in two passes
+// over the chunk's halves). P rows are padded by 16 bytes: 16 consecutive
+// heads read at one 16-byte column hit 16 distinct 4-bank groups.
+template <int G> constexpr int p_tokens() { return G == 64 ? kAttChunk / 2 : kAttChunk; }
+template <int G> constexpr int p_row_bytes() { return 2 * p_tokens<G>() + 16; }
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kRescaleSlack = 8.0f;
-constexpr int kGatherDepth = 4;   // gather lookahead in steps, 16- and 32-head groups
-constexpr int kGatherDepth64 = 2; // and 64-head groups
+static_assert(kMaxSteps == kAttWaves, "wave w gathers step w");
 
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef short shortx8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// G: heads per workgroup (16, 32 or 64; scoring waves past G / 16 idle).
-// Each head's arithmetic is the same whichever heads share its workgroup (a
-// head whose reference did not move rescales by exactly 1), so G changes
-// where the work runs, never a result.
-// kv carries no __restrict__: loads through a const restrict pointer count as
-// invariant, and the compiler then sinks the prologue's gathers past the
-// barriers to just before their use, where the stage waits a full memory
-// round trip for them.
+// Byte offset, inside a step tile, of 16-byte chunk `chunk` (0..31) of token
+// row `row` (0..31): rows are 512 bytes apart and their chunks XOR-swizzled
+// by the row index.
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kLat + ((chunk ^ row) << 4); }
+
+// Eight E4M3 bytes (two dwords) -> eight bf16, exact, in byte order.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(v2i w)
+{
+    u32x4 r;
+    r.x = e4m3x2_to_bf16x2_exact<false>((uint32_t)w.x);
+    r.y = e4m3x2_to_bf16x2_exact<true>((uint32_t)w.x);
+    r.z = e4m3x2_to_bf16x2_exact<false>((uint32_t)w.y);
+    r.w = e4m3x2_to_bf16x2_exact<true>((uint32_t)w.y);
+    return as_bf16x8(r);
+}
+
+// G: heads per workgroup (16, 32 or 64); it changes where the work runs,
+// never a result.
 template <int G>
 __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
-    const uint16_t *__restrict__ q, const uint8_t *kv,
+    const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
     const int32_t *__restrict__ bt, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ sel, uint16_t *__restrict__ part_o, float2 *__restrict__ part_ml,
     uint16_t *__restrict__ out, int K, int H, int top_k, int ps, int max_blocks, int num_pages,
     int max_len, float kv_scale, float qk_log2, int nch_max, int hg_count)
 {
-    __shared__ u32x4 tile[kTiles][kStep * kRowStride];   // bf16 tokens x latent, padded rows
-    __shared__ __align__(16) uint8_t pbuf[2][G * kPRowBytes]; // bf16 P, PV k order
-    __shared__ __align__(16) float alds[2][G];   // per-head rescale factors
-    __shared__ float2 mlds[G];                   // per-head (m, l) at the end
-    __shared__ int rowidx[kAttChunk];                    // latent row of each slot, -1 = skip
-    __shared__ int resc[kMaxSteps];                      // step s: O needs its alphas
+    constexpr int kHt = G / 16;                 // 16-head tiles of the group
+    constexpr int kWavesPerHt = kAttWaves / kHt; // QK: waves sharing one head tile (8, 4, 2)
+    constexpr int kTpw = kTokTiles / kWavesPerHt; // QK: token tiles of one wave (2, 4, 8)
+    constexpr int kPTok = p_tokens<G>();         // tokens whose P is in LDS at once
+    constexpr int kPRowBytes = p_row_bytes<G>();
+    constexpr int kPasses = kAttChunk / kPTok;   // PV passes over the chunk (1, 1, 2)
+    constexpr int kStepsPerPass = kPTok / kStep;
+    static_assert(kHt == 1 || kHt == 2 || kHt == 4, "16, 32 or 64 heads");
+    __shared__ __align__(16) uint8_t ring[kMaxSteps * kTileBytes]; // FP8 step tiles (128 KiB)
+    // bf16 P of one pass; with 16 heads it first holds the group's query
+    // (16 heads x 1 KiB, loaded once instead of once per wave)
+    constexpr int kQLds = kHt == 1;
+    constexpr int kPBytes = G * kPRowBytes;
+    __shared__ __align__(16) uint8_t pbuf[kQLds && 16 * 2 * kLat > kPBytes ? 16 * 2 * kLat : kPBytes];
+    __shared__ float wmax[kAttWaves][16];       // per-wave maxima of its head tile's heads
+    __shared__ float tsum[kTokTiles][G];        // per-token-tile sums of p
+    __shared__ __align__(16) uint8_t vmask[kAttChunk]; // slot holds a selected token
 
-    constexpr int kHt = G / 16; // 16-head MFMA tiles of the group
-    // steps of gathers in flight: as deep as the accumulators leave registers
-    // for (each step is 16 VGPRs per accumulating lane; 64 heads keep 128 in O)
-    constexpr int kDepth = G == 64 ? kGatherDepth64 : kGatherDepth;
-    static_assert(kHt >= 1 && kHt <= 4, "one scoring wave per 16 heads");
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
@@ -102,6 +121,34 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     const int c = blockIdx.x % nch_max;
     const int hg = blockIdx.x / nch_max;
     const int s = r / K;
+    const int slot0 = c * kAttChunk;
+    // The row length and this lane's selected id are requested together
+    // (the id's index is in bounds whatever the length: chunk c exists for
+    // top_k, and past the row's n the id is loaded but not used); the
+    // block-table lookup follows, and only then the query, so that neither
+    // resolution load waits behind the query's in the in-order return queue.
+    const int slot = kStep * wave + (lane & 31); // wave w resolves step w (both half-waves)
+    // QK ownership. A lane past the group's last head scores with head H-1's
+    // query: its results are never stored, and a head's arithmetic never
+    // involves another head's.
+    const int ht = wave / kWavesPerHt;           // head tile of this wave's QK
+    const int tt0 = (wave % kWavesPerHt) * kTpw; // its first token tile
+    const int hl = ht * 16 + n16;                // this lane's head within the group
+    if constexpr (kQLds) {
+        // 16 heads: wave w copies heads 2 w and 2 w + 1 (1 KiB each) into LDS
+        // first (no dependence on anything); the 16-byte chunk c of head h
+        // sits in slot c ^ (h & 15), so the 16 heads read at one column hit
+        // 16 distinct bank groups (lane j fetches the chunk its slot j holds)
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int hq = 2 * wave + i;
+            const uint8_t *gsrc = (const uint8_t *)(q + ((int64_t)r * H + min(hg * G + hq, H - 1)) * kLat) +
+                                  16 * (lane ^ (hq & 15));
+            __builtin_amdgcn_global_load_lds((const void *)gsrc, (lds_void *)(pbuf + hq * 2 * kLat), 16,
+                                             0, 0);
+        }
+    }
+    const int t_sel = sel[(int64_t)r * top_k + min(slot0 + slot, top_k - 1)];
     const int L = min(max(seq_lens[r], 0), max_len);
     const int n = min(top_k, L);
     const int nch = (n + kAttChunk - 1) / kAttChunk;
@@ -120,354 +167,249 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     }
     if (c >= nch)
         return;
-    const int slot0 = c * kAttChunk;
     const int nslots = min(n - slot0, kAttChunk);
-    const int nsteps = (nslots + kStep - 1) / kStep;
 
-    // ---- resolve the chunk's selected tokens to latent rows once ----
-    for (int k = tid; k < kAttChunk; k += kAttThreads) {
-        int row = -1;
-        if (k < nslots) {
-            const int t = sel[(int64_t)r * top_k + slot0 + k];
-            if (t >= 0 && t < L) {
-                const int page = bt[(int64_t)s * max_blocks + t / ps];
-                if (page >= 0 && page < num_pages)
-                    row = page * ps + t % ps;
-            }
-        }
-        rowidx[k] = row;
+    // ================= phase 1: resolve and gather step `wave` =================
+    int row = -1;
+    if (slot < nslots && t_sel >= 0 && t_sel < L) {
+        const int page = bt[(int64_t)s * max_blocks + t_sel / ps];
+        if (page >= 0 && page < num_pages)
+            row = page * ps + t_sel % ps;
     }
-    if (tid < kMaxSteps)
-        resc[tid] = 0;
-    // P rows of heads that no scoring wave covers stay zero
-    for (int i = tid; i < 2 * G * kPRowBytes / 16; i += kAttThreads)
-        ((u32x4 *)pbuf)[i] = u32x4{0u, 0u, 0u, 0u};
 
-    if (wave < 4) {
-        // ================= scoring waves: QK + online softmax =================
-        const int hl = wave * 16 + n16; // this lane's head within the group
-        const bool active = wave < kHt && wave * 16 < nh;
-        // query of head hl, latent dims 32 ks + 8 g .. +7 (the B operand).
-        // A lane past the group's last head scores with head H-1's query:
-        // its results are never stored, and it cannot change another head's
-        // (its reference moves exactly when head H-1's does, and an unmoved
-        // head rescales by exactly 1). Nothing reads the loads before the
-        // first product, so they stay in flight through the prologue.
-        u32x4 qr[16];
-        if (active) {
-            const uint16_t *qrow = q + ((int64_t)r * H + min(h0 + hl, H - 1)) * kLat + 8 * g;
+    // 32 or 64 heads: the query goes to registers, requested after the
+    // block-table lookup so that neither resolution load waits behind it
+    u32x4 qr[16]; // head hl, latent dims 32 ks + 8 g .. +7 (the B operand)
+    if constexpr (!kQLds) {
+        const uint16_t *qrow = q + ((int64_t)r * H + min(h0 + hl, H - 1)) * kLat + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < 16; ks++)
-                qr[ks] = *(const u32x4 *)(qrow + 32 * ks);
+        for (int ks = 0; ks < 16; ks++)
+            qr[ks] = *(const u32x4 *)(qrow + 32 * ks);
+    }
+
+    if (lane < 32)
+        vmask[slot] = row >= 0 ? 1 : 0;
+    if constexpr (kQLds) {
+        // the query copies (issued before the resolution loads, so drained
+        // with them) are published; the query goes to registers before any
+        // tile load is issued
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++)
+            qr[ks] = *(const u32x4 *)(pbuf + n16 * 2 * kLat + 16 * ((4 * ks + g) ^ n16));
+    }
+    {
+        uint8_t *tile = ring + wave * kTileBytes;
+        // A skipped slot (past the chunk, or out of contract) copies one of
+        // the step's selected rows instead: finite data that its zero
+        // probability removes exactly, and never a read of the skipped
+        // token. A step with no selected row is zeroed.
+        const uint64_t any = __ballot(row >= 0) & 0xFFFFFFFFull;
+        if (any != 0) {
+            const int sub = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)any) - 1);
+            const int src = row >= 0 ? row : sub;
+            const int half = lane >> 5;
+            // load i: tile rows 2 i (lanes 0-31) and 2 i + 1 (lanes 32-63);
+            // lane j fetches the global chunk that lands in slot j & 31 of
+            // its row (the swizzle's inverse)
+#pragma unroll
+            for (int i = 0; i < kDmaPerStep; i++) {
+                const int rowa = __builtin_amdgcn_readlane(src, 2 * i);
+                const int rowb = __builtin_amdgcn_readlane(src, 2 * i + 1);
+                const int trow = 2 * i + half;
+                const int grow = half ? rowb : rowa;
+                const uint8_t *gsrc = kv + (int64_t)grow * kLat + 16 * ((lane & 31) ^ trow);
+                __builtin_amdgcn_global_load_lds((const void *)gsrc, (lds_void *)(tile + 2 * i * kLat),
+                                                 16, 0, 0);
+            }
+        } else {
+            for (int i = lane; i < kTileBytes / 16; i += kWave)
+                *(u32x4 *)(tile + 16 * i) = u32x4{0u, 0u, 0u, 0u};
         }
-        float m_run = kNegInf; // reference max of the log2-domain logits (head hl)
-        float l_run = 0.0f;    // this lane's share of sum exp2(z - m_run)
+    }
+    if constexpr (kQLds) {
+        // a wave's two token tiles are its own step: its loads landing is
+        // enough (P overwrites the query area only after the maxima barrier,
+        // which every wave reaches after its QK has consumed the query)
+        __builtin_amdgcn_s_waitcnt(0xc07f & ~(0x3 << 14) & ~0xF); // vmcnt(0)
+    } else {
+        __syncthreads(); // every tile landed (each wave drained its own loads), masks set
+    }
 
-        // QK and online softmax of one step; leaves P and the alphas in
-        // buffer step & 1 and marks the step when a reference moved
-        auto qk_softmax = [&](int step) {
-            const u32x4 *tb = tile[step % kTiles];
-            floatx4 sacc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
-            // A: tile rows n16 and 16 + n16, k = latent dims 32 ks + 8 g .. +7.
-            // Software-pipelined in groups of four k-steps: the operands of
-            // group k0 + 1 are requested before the products of group k0, so
-            // the LDS latency hides behind the matrix core.
-            const u32x4 *t0row = tb + n16 * kRowStride + g;
-            const u32x4 *t1row = tb + (16 + n16) * kRowStride + g;
-            u32x4 a[2][8];
+    // ================= phase 2: QK and the chunk's maxima =================
+    // lane: head hl, tokens 16 tt + 4 g + v of each of its token tiles
+    floatx4 z[kTpw];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                a[0][2 * j] = t0row[4 * j];
-                a[0][2 * j + 1] = t1row[4 * j];
+    for (int j = 0; j < kTpw; j += 2) {
+        floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+        const int tt = tt0 + j; // even: tiles tt, tt + 1 are the two halves of step tt / 2
+        const uint8_t *tb = ring + (tt >> 1) * kTileBytes;
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+            v2i a[2][4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const int chunk = 2 * (k0 + k) + (g >> 1);
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+                    a[h][k] = *(const v2i *)(tb + tile_off(16 * h + n16, chunk) + 8 * (g & 1));
             }
 #pragma unroll
-            for (int k0 = 0; k0 < 4; k0++) {
-                if (k0 + 1 < 4) {
+            for (int k = 0; k < 4; k++) {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        a[(k0 + 1) & 1][2 * j] = t0row[4 * (4 * (k0 + 1) + j)];
-                        a[(k0 + 1) & 1][2 * j + 1] = t1row[4 * (4 * (k0 + 1) + j)];
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    sacc[0] = mfma16x16x32(as_bf16x8(a[k0 & 1][2 * j]), as_bf16x8(qr[4 * k0 + j]), sacc[0]);
-                    sacc[1] = mfma16x16x32(as_bf16x8(a[k0 & 1][2 * j + 1]), as_bf16x8(qr[4 * k0 + j]), sacc[1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int h = 0; h < 2; h++)
+                    acc[h] = mfma16x16x32(fp8x8_to_bf16x8(a[h][k]), as_bf16x8(qr[k0 + k]), acc[h]);
             }
-            // lane: head hl, tokens 16*(j>>2) + 4g + (j&3) for j = 0..7
-            float z[8];
-            float mx = kNegInf;
+        }
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const float v = sacc[j >> 2][j & 3] * qk_log2;
-                z[j] = rowidx[step * kStep + 16 * (j >> 2) + 4 * g + (j & 3)] >= 0 ? v : kNegInf;
-                mx = __builtin_fmaxf(mx, z[j]);
-            }
-            mx = max_xor32(max_xor16(mx));
-            // The reference max moves only when the step's max exceeds it by
-            // more than kRescaleSlack (log2 units): then p <= 2^kRescaleSlack,
-            // so fp32 sums and bf16 probabilities stay well scaled, and O is
-            // rescaled only on rare steps. The rule is a function of the row's
-            // data alone, so results stay bit-reproducible; the partial state
-            // (m_ref, l, O) merges exactly as with the true max.
-            const bool move = mx > m_run + kRescaleSlack;
-            const float m_new = move ? mx : m_run;
-            const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-            const float alpha = exp2f(m_run - m_use);
-            float p[8];
-            float rs = 0.0f;
+        for (int h = 0; h < 2; h++) {
+            const uint32_t mw = *(const uint32_t *)(vmask + 16 * (tt + h) + 4 * g);
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                p[j] = exp2f(z[j] - m_use);
-                rs += p[j];
-            }
-            l_run = __builtin_fmaf(l_run, alpha, rs);
+            for (int v = 0; v < 4; v++)
+                z[j + h][v] = ((mw >> (8 * v)) & 0xFFu) ? acc[h][v] * qk_log2 : kNegInf;
+        }
+    }
+    {
+        float mx = kNegInf;
+#pragma unroll
+        for (int j = 0; j < kTpw; j++)
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                mx = __builtin_fmaxf(mx, z[j][v]);
+        mx = max_xor32(max_xor16(mx));
+        if (g == 0)
+            wmax[wave][n16] = mx;
+    }
+    __syncthreads(); // wave maxima
+
+    // ================= phase 3: softmax over the chunk =================
+    float m = kNegInf; // the chunk's largest logit of head hl (exact: order-free)
+#pragma unroll
+    for (int w = 0; w < kWavesPerHt; w++)
+        m = __builtin_fmaxf(m, wmax[ht * kWavesPerHt + w][n16]);
+    const float m_use = (m == kNegInf) ? 0.0f : m;
+    u32x4 pk[kTpw / 2]; // bf16 P of each of this wave's steps, PV k order
+#pragma unroll
+    for (int j = 0; j < kTpw; j += 2) {
+        float p[8];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                p[4 * h + v] = exp2f(z[j + h][v] - m_use);
+            // tile sum: this lane's four tokens, then the four lane groups,
+            // in one fixed order (the swaps add commuted pairs: same bits)
+            float ts = (p[4 * h] + p[4 * h + 1]) + (p[4 * h + 2] + p[4 * h + 3]);
+            ts = add_xor32(add_xor16(ts));
             if (g == 0)
-                alds[step & 1][hl] = alpha;
-            if (__ballot(move && m_run != kNegInf) != 0 && lane == 0)
-                resc[step] = 1;
-            m_run = m_new;
-            u32x4 pw;
-            pw.x = pack_bf16x2(p[0], p[1]);
-            pw.y = pack_bf16x2(p[2], p[3]);
-            pw.z = pack_bf16x2(p[4], p[5]);
-            pw.w = pack_bf16x2(p[6], p[7]);
-            *(u32x4 *)(pbuf[step & 1] + hl * kPRowBytes + 16 * g) = pw;
-        };
-
-        __syncthreads(); // rowidx, resc cleared
-        __syncthreads(); // tile 0 staged
-        if (active)
-            qk_softmax(0);
-        __syncthreads(); // P of step 0, tile 1 staged
-        for (int i = 0; i < nsteps; i++) {
-            if (active && i + 1 < nsteps)
-                qk_softmax(i + 1);
-            __syncthreads();
+                tsum[tt0 + j + h][hl] = ts;
         }
-        // per-head (m, l): the four lanes of a head hold shares of l
-        const float l_all = add_xor32(add_xor16(l_run));
-        if (active && g == 0) {
-            mlds[hl] = float2{m_run, l_all};
-            if (nch > 1) {
-                const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * G;
-                part_ml[pbase + hl] = float2{m_run, l_all};
-            }
-        }
-        __syncthreads(); // mlds
-        return;
+        pk[j / 2].x = pack_bf16x2(p[0], p[1]);
+        pk[j / 2].y = pack_bf16x2(p[2], p[3]);
+        pk[j / 2].z = pack_bf16x2(p[4], p[5]);
+        pk[j / 2].w = pack_bf16x2(p[6], p[7]);
     }
 
-    // ================= accumulating waves: gather, stage, PV =================
-    const int v = wave - 4;
-    const int ptid = tid - 4 * kWave; // 0..255
-    const int tq = ptid >> 5;         // staging: tokens 4 tq .. 4 tq + 3
-    const int dc = ptid & 31;         //          latent bytes 16 dc .. 16 dc + 15
-    floatx4 o[kHt][kPvTiles]; // O[head 16 mt + n16][columns kPvCols v + 16 nt + 4 g + e]
+    // ================= phase 4: PV =================
+    // The tile as A through 8-bit transpose reads: in lane group g, lane
+    // pair k supplies token row 4 g + k (k < 4) or 16 + 4 g + k - 4, so lane
+    // n16 receives column 16 (4 wave + i) + n16 of those 8 rows (k-slot j <->
+    // token 16 (j >> 2) + 4 g + (j & 3) of the step, the order P is written
+    // in); P as B. A lane ends with 4 consecutive columns of one head.
+    const int kp = n16 >> 1;
+    const int trrow = (kp < 4) ? 4 * g + kp : 16 + 4 * g + (kp - 4);
+    floatx4 o[kHt][kPvColTiles]; // O^T[cols 64 wave + 16 i + 4 g + e][head 16 mt + n16]
+    float lh[kHt];               // l of head 16 mt + n16
 #pragma unroll
     for (int mt = 0; mt < kHt; mt++)
 #pragma unroll
-        for (int nt = 0; nt < kPvTiles; nt++)
-            o[mt][nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // One step's 32 FP8 rows into registers (slot indices first, then the
-    // four loads back to back; a skipped slot reads latent row 0 and is
-    // zeroed when staged, so nothing waits on the loads here).
-    auto gather = [&](u32x4 (&raw)[4], int step) {
-        int row[4];
+        for (int i = 0; i < kPvColTiles; i++)
+            o[mt][i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int k = step * kStep + 4 * tq + i;
-            row[i] = (k < kAttChunk) ? rowidx[k] : -1;
+    for (int pass = 0; pass < kPasses; pass++) {
+        if (pass > 0)
+            __syncthreads(); // the previous pass's P reads are done
+        // this wave's P of the pass's steps
+#pragma unroll
+        for (int j = 0; j < kTpw; j += 2) {
+            const int st = (tt0 + j) >> 1;
+            if (st / kStepsPerPass == pass)
+                *(u32x4 *)(pbuf + hl * kPRowBytes + 2 * (kStep * (st % kStepsPerPass) + 8 * g)) = pk[j / 2];
         }
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            raw[i] = *(const u32x4 *)(kv + (int64_t)max(row[i], 0) * kLat + 16 * dc);
-    };
-    // Dequantise (exact) into the tile of `step`.
-    auto stage = [&](const u32x4 (&raw)[4], int step) {
-        u32x4 *tb = tile[step % kTiles];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int t = 4 * tq + i;
-            const int k = step * kStep + t;
-            const bool skip = k >= kAttChunk || rowidx[k] < 0;
-            const u32x4 w = skip ? u32x4{0u, 0u, 0u, 0u} : raw[i];
-            u32x4 lo, hi;
-            lo.x = e4m3x2_to_bf16x2_exact<false>(w.x);
-            lo.y = e4m3x2_to_bf16x2_exact<true>(w.x);
-            lo.z = e4m3x2_to_bf16x2_exact<false>(w.y);
-            lo.w = e4m3x2_to_bf16x2_exact<true>(w.y);
-            hi.x = e4m3x2_to_bf16x2_exact<false>(w.z);
-            hi.y = e4m3x2_to_bf16x2_exact<true>(w.z);
-            hi.z = e4m3x2_to_bf16x2_exact<false>(w.w);
-            hi.w = e4m3x2_to_bf16x2_exact<true>(w.w);
-            // lanes dc and dc + 8 would hit the same banks with the chunk
-            // pair in order; the upper eight of every sixteen write it swapped
-            const int sw = (dc >> 3) & 1;
-            tb[t * kRowStride + 2 * dc + sw] = sw ? hi : lo;
-            tb[t * kRowStride + 2 * dc + 1 - sw] = sw ? lo : hi;
-        }
-    };
-    // PV of one step, transposed: O^T[this wave's columns, heads] += V^T P^T.
-    // The tile as A through two transpose loads of 4 consecutive rows each
-    // (lane n16 receives column kPvCols v + 16 nt + n16, rows 4g..4g+3 and
-    // 16+4g..16+4g+3, i.e. k-slot j <-> token 16(j>>2) + 4g + (j&3)), P as B
-    // in the same k order. A lane ends with 4 consecutive columns of one
-    // head: one rescale factor per head tile, 8-byte output stores.
-    auto pv = [&](int step) {
-        const bool rs = resc[step] != 0;
-        const char *tb = (const char *)tile[step % kTiles];
-        const uint8_t *pb = pbuf[step & 1];
-        const char *p0 = tb + (4 * g + (n16 >> 2)) * (kRowStride * 16) + 8 * (n16 & 3) +
-                         2 * kPvCols * v;
-        const char *p1 = p0 + 16 * (kRowStride * 16);
-        if (rs) {
+        __syncthreads(); // P of the pass (and, at the first, every tile sum)
+        if (pass == 0) {
+            // l of each head: the token-tile sums in tile order
 #pragma unroll
             for (int mt = 0; mt < kHt; mt++) {
-                const float a = alds[step & 1][16 * mt + n16];
+                float acc = 0.0f;
 #pragma unroll
-                for (int nt = 0; nt < kPvTiles; nt++) {
-                    o[mt][nt][0] *= a;
-                    o[mt][nt][1] *= a;
-                    o[mt][nt][2] *= a;
-                    o[mt][nt][3] *= a;
-                }
+                for (int tt = 0; tt < kTokTiles; tt++)
+                    acc += tsum[tt][16 * mt + n16];
+                lh[mt] = acc;
+            }
+            if (nch > 1 && wave % kWavesPerHt == 0 && g == 0 && hl < nh) {
+                const int64_t pb = (((int64_t)r * hg_count + hg) * nch_max + c) * G;
+                part_ml[pb + hl] = float2{m, lh[ht]};
             }
         }
-        // every operand of the step is requested before the first product
-        bf16x8 pa[4];
 #pragma unroll
-        for (int mt = 0; mt < kHt; mt++)
-            pa[mt] = as_bf16x8(*(const u32x4 *)(pb + (16 * mt + n16) * kPRowBytes + 16 * g));
-        shortx8 vb[kPvTiles];
+        for (int sp = 0; sp < kStepsPerPass; sp++) {
+            const int st = pass * kStepsPerPass + sp;
+            const uint8_t *tb = ring + st * kTileBytes;
+            v2i raw[kPvColTiles];
 #pragma unroll
-        for (int nt = 0; nt < kPvTiles; nt++) {
-            const shortx4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p0 + 32 * nt));
-            const shortx4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(p1 + 32 * nt));
-            vb[nt] = shortx8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        }
-        __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < kPvColTiles; i++)
+                raw[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (lds_v2i *)(tb + tile_off(trrow, kPvColTiles * wave + i) + 8 * (n16 & 1)));
+            bf16x8 pa[kHt];
 #pragma unroll
-        for (int nt = 0; nt < kPvTiles; nt++) {
+            for (int mt = 0; mt < kHt; mt++)
+                pa[mt] = as_bf16x8(*(const u32x4 *)(pbuf + (mt * 16 + n16) * kPRowBytes +
+                                                    2 * (kStep * sp + 8 * g)));
 #pragma unroll
-            for (int mt = 0; mt < kHt; mt++) // head tiles past the group's heads see P = 0
-                o[mt][nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vb[nt]), pa[mt], o[mt][nt]);
-        }
-    };
-
-    __syncthreads(); // rowidx, resc cleared
-    // Gathers run kDepth steps ahead: buffer j % kDepth holds step j's rows
-    // from the step that issues its loads until the step that stages it.
-    // Step 0 is staged before the scoring waves start and step 1 while they
-    // score it; step i + 2 is staged during step i, and its buffer then
-    // takes the loads of step i + 2 + kDepth.
-    // Prologue gathers are issued whatever the chunk's step count (a step
-    // past the chunk reads latent row 0 and is never staged). With 16- and
-    // 32-head groups the step loop is unrolled (at most kMaxSteps steps), so
-    // every buffer index is a constant and the loads outstanding at each
-    // stage are the same on every path: the compiler's wait before a stage
-    // then covers exactly that step's loads, not the later steps' still in
-    // flight (measured at 8 x 131072: a workgroup's span from 14.4 to 12.4 us).
-    u32x4 rbuf[kDepth][4];
+            for (int i = 0; i < kPvColTiles; i++) {
+                const bf16x8 va = fp8x8_to_bf16x8(raw[i]);
 #pragma unroll
-    for (int j = 0; j < kDepth; j++)
-        gather(rbuf[j], j);
-    __builtin_amdgcn_sched_barrier(0); // every prologue load issued before the first wait
-    stage(rbuf[0], 0);
-    __syncthreads(); // tile 0 staged
-    gather(rbuf[0], kDepth);
-    if (nsteps > 1)
-        stage(rbuf[1], 1);
-    gather(rbuf[1 % kDepth], kDepth + 1);
-    __syncthreads(); // P of step 0, tile 1 staged
-    // step i: PV of step i and staging of step i + 2, while the scoring
-    // waves score step i + 1
-    if constexpr (G == 64) {
-        // A rolled loop (unrolled, the 64-head accumulators and the rows in
-        // flight need more registers than a wave has): the buffer of a step
-        // is picked at run time, and a gather is issued only for a step the
-        // chunk has.
-        for (int i = 0; i < nsteps; i++) {
-            if (i + 2 < nsteps) {
-#pragma unroll
-                for (int b = 0; b < kDepth; b++) {
-                    if (b == (i + 2) % kDepth) {
-                        stage(rbuf[b], i + 2);
-                        if (i + 2 + kDepth < nsteps)
-                            gather(rbuf[b], i + 2 + kDepth);
-                    }
-                }
+                for (int mt = 0; mt < kHt; mt++) // head tiles past the group's heads see P = 0
+                    o[mt][i] = mfma16x16x32(va, pa[mt], o[mt][i]);
             }
-            pv(i);
-            __syncthreads();
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kMaxSteps; i++) {
-            if (i >= nsteps)
-                break;
-            if (i + 2 < nsteps)
-                stage(rbuf[(i + 2) % kDepth], i + 2);
-            // steps past kMaxSteps are dropped at compile time; one past the
-            // chunk's last step is a wasted read of latent row 0
-            if (i + 2 + kDepth < kMaxSteps)
-                gather(rbuf[(i + 2) % kDepth], i + 2 + kDepth);
-            pv(i);
-            __syncthreads();
         }
     }
-    __syncthreads(); // mlds
 
-    // Output through LDS: each wave parks its O block (G heads x its 128
-    // columns, bf16) in its own region of the now idle tiles, then writes it
-    // back as whole 256-byte head rows with 16-byte stores. Only this wave
-    // touches its region, so a wait for its own LDS writes is enough.
-    constexpr int kORowBytes = 2 * kPvCols + 16; // padded: 16 rows at one column spread over the banks
-    static_assert(4 * G * kORowBytes <= (int)sizeof(tile), "O blocks fit the tiles");
-    uint8_t *oreg = (uint8_t *)tile + v * (G * kORowBytes);
+    __syncthreads(); // every wave is done with the ring
+
+    // Output through LDS: the waves park O (G heads x 512 columns, bf16) in
+    // the idle ring, then write it back as whole 1 KiB head rows with 16-byte
+    // stores (measured faster than 8-byte stores straight from registers).
+    constexpr int kORowBytes = 2 * kLat + 16; // padded: 16 rows at one column spread over the banks
+    static_assert(G * kORowBytes <= (int)sizeof(ring), "O fits the ring");
+#pragma unroll
+    for (int mt = 0; mt < kHt; mt++) {
+        const float sc = (nch == 1) ? (lh[mt] > 0.0f ? kv_scale / lh[mt] : 0.0f) : 1.0f;
+#pragma unroll
+        for (int i = 0; i < kPvColTiles; i++) {
+            u32x2 pw;
+            pw.x = pack_bf16x2(o[mt][i][0] * sc, o[mt][i][1] * sc);
+            pw.y = pack_bf16x2(o[mt][i][2] * sc, o[mt][i][3] * sc);
+            *(u32x2 *)(ring + (16 * mt + n16) * kORowBytes + 2 * (16 * (kPvColTiles * wave + i) + 4 * g)) = pw;
+        }
+    }
+    __syncthreads();
     const int64_t pbase = (((int64_t)r * hg_count + hg) * nch_max + c) * G;
-    auto park = [&](auto scale_of) {
 #pragma unroll
-        for (int mt = 0; mt < kHt; mt++) {
-            const int hl = 16 * mt + n16;
-            const float sc = scale_of(hl);
-#pragma unroll
-            for (int nt = 0; nt < kPvTiles; nt++) {
-                u32x2 pk;
-                pk.x = pack_bf16x2(o[mt][nt][0] * sc, o[mt][nt][1] * sc);
-                pk.y = pack_bf16x2(o[mt][nt][2] * sc, o[mt][nt][3] * sc);
-                *(u32x2 *)(oreg + hl * kORowBytes + 2 * (16 * nt + 4 * g)) = pk;
-            }
-        }
-    };
-    if (nch == 1) { // the final output: O / l, with kv_scale
-        park([&](int hl) {
-            const float lh = mlds[hl].y;
-            return lh > 0.0f ? kv_scale / lh : 0.0f;
-        });
-    } else {        // a partial: O as accumulated
-        park([](int) { return 1.0f; });
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // lane: 16 bytes (8 columns) of head row 4 i + (lane >> 4)
-    const int cb = 16 * (lane & 15);
-#pragma unroll
-    for (int i = 0; i < G / 4; i++) {
-        const int hl = 4 * i + (lane >> 4);
-        const int h = h0 + hl;
-        const u32x4 val = *(const u32x4 *)(oreg + hl * kORowBytes + cb);
-        if (hl < nh) {
-            uint16_t *orow = (nch == 1) ? out + ((int64_t)r * H + h) * kLat
-                                        : part_o + (pbase + hl) * kLat;
-            // streaming store: the partials are read once, by the merge
-            // (measured: -1 us per step at 8 x 131072 and 64 x 16.4k)
-            __builtin_nontemporal_store(val, (u32x4 *)((uint8_t *)(orow + kPvCols * v) + cb));
+    for (int it = 0; it < G * (kLat * 2 / 16) / kAttThreads; it++) {
+        const int e = it * kAttThreads + tid; // 16-byte piece e of the G x 1 KiB block
+        const int hrow = e / (kLat * 2 / 16);
+        const int cb = 16 * (e % (kLat * 2 / 16));
+        if (hrow < nh) {
+            const u32x4 val = *(const u32x4 *)(ring + hrow * kORowBytes + cb);
+            uint16_t *orow = (nch == 1) ? out + ((int64_t)r * H + h0 + hrow) * kLat
+                                        : part_o + (pbase + hrow) * kLat;
+            // streaming store for partials: read once, by the merge
+            if (nch == 1)
+                *(u32x4 *)((uint8_t *)orow + cb) = val;
+            else
+                __builtin_nontemporal_store(val, (u32x4 *)((uint8_t *)orow + cb));
         }
     }
 }
