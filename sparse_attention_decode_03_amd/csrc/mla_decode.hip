@@ -84,6 +84,61 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(v2i w)
     return as_bf16x8(r);
 }
 
+// Folding the per-chunk partials of one (row, head) at latent columns
+// d .. d + 3, strictly in chunk order 0, 1, 2, ... with one fp32 formula.
+// Partials are loaded in unrolled batches (independent loads in flight), then
+// folded; straight-line code with selects, so the batch stays in registers. A
+// batch is the chunk count of a row at top_k = 2048 (8 x 256 slots): a larger
+// one re-reads the last chunk (measured: 16 cost 3.5 us per step at
+// 64 x 16.4k).
+constexpr int kFoldBatch = 8;
+struct FoldState {
+    float m, l;
+    floatx4 acc;
+};
+struct FoldBatch {
+    float2 ml[kFoldBatch];
+    floatx4 ov[kFoldBatch];
+};
+// chunks past `last` re-read it (branch-free; they are not folded)
+__device__ __forceinline__ void fold_load(const uint16_t *part_o, const float2 *part_ml, int64_t pbase,
+                                          int G, int c0, int last, int d, FoldBatch &b)
+{
+#pragma unroll
+    for (int k = 0; k < kFoldBatch; k++) {
+        const int64_t pi = pbase + (int64_t)min(c0 + k, last) * G;
+        b.ml[k] = part_ml[pi];
+        const u32x2 pk = *(const u32x2 *)(part_o + pi * kLat + d);
+        b.ov[k] = floatx4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
+                          __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)};
+    }
+}
+__device__ __forceinline__ void fold_step(int c0, int nch, const FoldBatch &b, FoldState &f)
+{
+#pragma unroll
+    for (int k = 0; k < kFoldBatch; k++) {
+        const float m_new = __builtin_fmaxf(f.m, b.ml[k].x);
+        // a chunk past the last, or one with nothing selected so far, leaves
+        // the state untouched
+        const bool use = (c0 + k < nch) && (m_new != kNegInf);
+        const float a = use ? exp2f(f.m - m_new) : 1.0f;
+        const float e = use ? exp2f(b.ml[k].x - m_new) : 0.0f;
+        f.l = use ? __builtin_fmaf(b.ml[k].y, e, f.l * a) : f.l;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            f.acc[i] = use ? __builtin_fmaf(b.ov[k][i], e, f.acc[i] * a) : f.acc[i];
+        f.m = use ? m_new : f.m;
+    }
+}
+__device__ __forceinline__ u32x2 fold_output(const FoldState &f, float kv_scale)
+{
+    const float inv = f.l > 0.0f ? kv_scale / f.l : 0.0f;
+    u32x2 packed;
+    packed.x = pack_bf16x2(f.acc[0] * inv, f.acc[1] * inv);
+    packed.y = pack_bf16x2(f.acc[2] * inv, f.acc[3] * inv);
+    return packed;
+}
+
 // G: heads per workgroup (16, 32 or 64); it changes where the work runs,
 // never a result.
 template <int G>
@@ -414,10 +469,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     }
 }
 
-// Fold the per-chunk partials of every (row, head) in chunk order.
-// (the partial pointers carry no __restrict__, so the first batch's loads are
+// Fold the per-chunk partials of every (row, head).
+// The partial pointers carry no __restrict__, so the first batch's loads are
 // not sunk below the row-length test: loads through const restrict pointers
-// count as invariant and move freely)
+// count as invariant and move freely.
 __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *part_o,
                                                    const float2 *part_ml,
                                                    const int32_t *__restrict__ seq_lens,
@@ -431,60 +486,23 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *part_o,
     const int hl = h % G;
     const int d = threadIdx.x * 4;
     const int64_t pbase = ((int64_t)r * hg_count + hg) * nch_max * G + hl;
-    // partials are loaded in unrolled batches (independent loads in flight),
-    // then folded strictly in chunk order; straight-line code with selects,
-    // so the batch stays in registers. A batch is the chunk count of a row
-    // at top_k = 2048 (8 x 256 slots): a larger one re-reads the last chunk
-    // (measured: 16 cost 3.5 us per step at 64 x 16.4k)
-    constexpr int kB = 8;
-    float2 ml[kB];
-    floatx4 ov[kB];
-    // branch-free: chunks past the last re-read it (and are not folded)
-    auto load_batch = [&](int c0, int last) {
-#pragma unroll
-        for (int k = 0; k < kB; k++) {
-            const int64_t pi = pbase + (int64_t)min(c0 + k, last) * G;
-            ml[k] = part_ml[pi];
-            const u32x2 pk = *(const u32x2 *)(part_o + pi * kLat + d);
-            ov[k] = floatx4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
-                            __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)};
-        }
-    };
+    FoldBatch b;
     // the first batch goes out before the row's chunk count is known (every
     // chunk up to nch_max has its place in the workspace)
-    load_batch(0, nch_max - 1);
+    fold_load(part_o, part_ml, pbase, G, 0, nch_max - 1, d, b);
     __asm__ volatile("" ::: "memory"); // those loads stay ahead of the length load and test
     const int L = min(max(seq_lens[r], 0), max_len);
     const int n = min(top_k, L);
     const int nch = (n + kAttChunk - 1) / kAttChunk;
     if (nch <= 1)
         return;
-    float m_acc = kNegInf, l_acc = 0.0f;
-    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c0 = 0; c0 < nch; c0 += kB) {
+    FoldState f{kNegInf, 0.0f, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int c0 = 0; c0 < nch; c0 += kFoldBatch) {
         if (c0 > 0)
-            load_batch(c0, nch - 1);
-#pragma unroll
-        for (int k = 0; k < kB; k++) {
-            const float m_new = __builtin_fmaxf(m_acc, ml[k].x);
-            // a chunk past the last, or one with nothing selected so far,
-            // leaves the state untouched
-            const bool use = (c0 + k < nch) && (m_new != kNegInf);
-            const float a = use ? exp2f(m_acc - m_new) : 1.0f;
-            const float b = use ? exp2f(ml[k].x - m_new) : 0.0f;
-            l_acc = use ? __builtin_fmaf(ml[k].y, b, l_acc * a) : l_acc;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                acc[i] = use ? __builtin_fmaf(ov[k][i], b, acc[i] * a) : acc[i];
-            m_acc = use ? m_new : m_acc;
-        }
+            fold_load(part_o, part_ml, pbase, G, c0, nch - 1, d, b);
+        fold_step(c0, nch, b, f);
     }
-    const float inv = l_acc > 0.0f ? kv_scale / l_acc : 0.0f;
-    uint16_t *orow = out + ((int64_t)r * H + h) * kLat + d;
-    u32x2 packed;
-    packed.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    packed.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *(u32x2 *)orow = packed;
+    *(u32x2 *)(out + ((int64_t)r * H + h) * kLat + d) = fold_output(f, kv_scale);
 }
 
 // Compute units of the current device (cached per device).
