@@ -7,10 +7,13 @@ steps honest about HBM (the 256 MB Infinity Cache would otherwise hold much of
 the working set), the keys and the latent pool are replicated and the steps
 rotate through the replicas.
 
-Prints one JSON line. `roofline` covers the dominant kernel (the index-score
-pass): algorithmic bytes per launch over its mean duration, measured with HIP
-events on the stream it runs on. `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+Prints one JSON line. `roofline` covers the dominant kernel (the in-step
+index-score pass): algorithmic bytes per launch over its median duration,
+measured with HIP events recorded on the step's stream around it
+(dsa_decode_k_timed). `stage_us` gives the median of every stage the same
+way, and `index_attend_roofline` puts the step's algorithmic bytes over the
+indexer plus the gather-attend (attention and chunk merge). `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -246,10 +249,32 @@ def main() -> int:
         read_ceiling = 5 * big.numel() * 2 / (sa.elapsed_time(sb) * 1e-3) / 1e9
         del big
 
-        # dominant kernel: the index-score pass, launched back to back on
-        # rotating replicas (cold keys, as in the timed steps) between one
-        # pair of HIP events on the stream it runs on; the mean per launch
-        # is the span over the launch count (no per-launch event gaps)
+        # per-kernel times inside the step: the same steps through
+        # dsa_decode_k_timed, whose kernels are launched with start/stop HIP
+        # events bound to their own dispatches (index, filter, finish,
+        # attention, merge) on the step's stream
+        nst = min(args.steps, 100)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(nst)]
+        for evs6 in sev:
+            for e in evs6:
+                e.record(stream)  # creates the underlying event
+        torch.cuda.synchronize()
+        for i in range(nst):
+            dsa.decode_k_timed(sh, step.q_idx, step.w, keys[i % nrep], step.q, pools[i % nrep],
+                               step.block_tables, step.seq_lens, step.kv_scale, step.sm_scale,
+                               step.scores, step.sel, step.out, step.ws, sev[i], stream=stream)
+        torch.cuda.synchronize()
+        stage_names = ["index", "select_filter", "select_finish", "attend", "merge"]
+        stage_us = {nm: float(np.median([sev[i][2 * j].elapsed_time(sev[i][2 * j + 1]) * 1e3
+                                         for i in range(nst)]))
+                    for j, nm in enumerate(stage_names)}
+        stage_mean_us = {nm: float(np.mean([sev[i][2 * j].elapsed_time(sev[i][2 * j + 1]) * 1e3
+                                            for i in range(nst)]))
+                         for j, nm in enumerate(stage_names)}
+
+        # dominant kernel, standalone: the index-score pass launched back to
+        # back on rotating replicas between one pair of HIP events (a
+        # cross-check of the in-step figure; it writes no group maxima)
         ev_a = torch.cuda.Event(enable_timing=True)
         ev_b = torch.cuda.Event(enable_timing=True)
         dsa.index_scores(sh, step.q_idx, step.w, keys[1 % nrep], step.seq_lens, step.scores,
@@ -264,8 +289,14 @@ def main() -> int:
 
     ab = algorithmic_bytes(inputs)
     ms = elapsed / args.steps * 1e3
-    achieved = ab["index"] / (idx_ms * 1e-3) / 1e9
+    idx_us = stage_us["index"]
+    achieved = ab["index"] / (idx_us * 1e-6) / 1e9
     traffic = load_traffic()
+    # the indexer plus the gather-attend (attention and chunk merge), against
+    # every algorithmic byte of the step (keys, selected rows, q/out,
+    # q_idx/w, block-table entries)
+    ia_us = stage_us["index"] + stage_us["attend"] + stage_us["merge"]
+    ia_gbs = ab["total"] / (ia_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": args.steps / elapsed,
@@ -288,12 +319,20 @@ def main() -> int:
             "parallelism": "single-gpu", "replicas": nrep,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "k_index_scores",
+            "bound": "hbm", "kernel": "k_index_scores (in-step: scores and group maxima)",
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab["index"],
-            "mean_launch_ms": idx_ms,
+            "median_launch_us": idx_us,
+            "mean_launch_us": stage_mean_us["index"],
+            "standalone_mean_launch_us": idx_ms * 1e3,
+        },
+        "stage_us": stage_us,
+        "index_attend_roofline": {
+            "stages": "index + attend + merge", "us": ia_us,
+            "algorithmic_bytes": ab["total"], "achieved_GBs": ia_gbs,
+            "peak_GBs": HBM_PEAK_GBS, "frac": ia_gbs / HBM_PEAK_GBS,
         },
         "step_roofline": {
             "algorithmic_bytes": ab["total"],

@@ -191,6 +191,22 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w,
                  size_t ws_bytes, void *stream);
 
 /*
+ * dsa_decode_k for measurement: the same kernels on the same stream, each
+ * launched with hipExtLaunchKernel and a start/stop pair of caller-created
+ * HIP events (hipEvent_t, created with timing), so that the span of a pair
+ * is that kernel's own run. events[0..9] are the pairs of the index pass,
+ * the selection's filter, its finish, the attention and the chunk merge;
+ * when no row has more than one chunk there is no merge and its two events
+ * are recorded right after the attention. Results are those of
+ * dsa_decode_k. Refusals as dsa_decode_k, and DSA_EINVAL for a NULL event.
+ */
+int dsa_decode_k_timed(const dsa_shape *shape, const void *q_idx, const float *w,
+                       const void *k_normed, const void *q, const uint8_t *kv_cache,
+                       const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
+                       float sm_scale, float *scores, int32_t *sel, void *out, void *ws,
+                       size_t ws_bytes, void *stream, void *const *events);
+
+/*
  * dsa_decode_k for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
  * same kernels and results as dsa_decode_k (byte for byte), with the

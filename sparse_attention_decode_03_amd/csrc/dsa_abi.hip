@@ -338,12 +338,18 @@ int dsa_mla_decode(const dsa_shape *shape, const void *q, const uint8_t *kv_cach
                     "mla_decode");
 }
 
-int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, const void *k_normed,
-                 const void *q, const uint8_t *kv_cache, const int32_t *block_tables,
-                 const int32_t *seq_lens, float kv_scale, float sm_scale, float *scores,
-                 int32_t *sel, void *out, void *ws, size_t ws_bytes, void *stream)
+} // extern "C"
+
+namespace {
+
+// The whole step. ev: null, or 10 events bound in start/stop pairs to the
+// index, filter, finish, attention and merge kernels.
+int decode_k_impl(const dsa_shape *shape, const void *q_idx, const float *w, const void *k_normed,
+                  const void *q, const uint8_t *kv_cache, const int32_t *block_tables,
+                  const int32_t *seq_lens, float kv_scale, float sm_scale, float *scores,
+                  int32_t *sel, void *out, void *ws, size_t ws_bytes, void *stream,
+                  hipEvent_t const *ev)
 {
-    g_err[0] = 0;
     dsa::LaunchShape ls;
     int rc;
     if ((rc = check_shape(shape, &ls)) != DSA_OK)
@@ -362,19 +368,59 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, cons
         return rc;
     hipStream_t st = (hipStream_t)stream;
     char *wsb = (char *)ws;
+    auto timer = [&](int stage) {
+        dsa::KTimer t;
+        if (ev != nullptr) {
+            t.start = ev[2 * stage];
+            t.stop = ev[2 * stage + 1];
+        }
+        return t;
+    };
     if ((rc = launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
                                                 (const uint16_t *)k_normed, seq_lens, scores,
                                                 (uint32_t *)(wsb + wl.gm4),
-                                                (uint32_t *)(wsb + wl.gm32), st),
+                                                (uint32_t *)(wsb + wl.gm32), st, timer(0)),
                        "index_scores")) ||
-        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, true, st),
+        (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, true, st, timer(1),
+                                          timer(2)),
                        "select")) ||
         (rc = launched(dsa::launch_mla_decode(ls, (const uint16_t *)q, kv_cache, block_tables,
                                               seq_lens, sel, kv_scale, sm_scale, (uint16_t *)out,
-                                              wsb, wl, st),
+                                              wsb, wl, st, timer(3), timer(4)),
                        "mla_decode")))
         return rc;
     return DSA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w, const void *k_normed,
+                 const void *q, const uint8_t *kv_cache, const int32_t *block_tables,
+                 const int32_t *seq_lens, float kv_scale, float sm_scale, float *scores,
+                 int32_t *sel, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    return decode_k_impl(shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_lens, kv_scale,
+                         sm_scale, scores, sel, out, ws, ws_bytes, stream, nullptr);
+}
+
+int dsa_decode_k_timed(const dsa_shape *shape, const void *q_idx, const float *w,
+                       const void *k_normed, const void *q, const uint8_t *kv_cache,
+                       const int32_t *block_tables, const int32_t *seq_lens, float kv_scale,
+                       float sm_scale, float *scores, int32_t *sel, void *out, void *ws,
+                       size_t ws_bytes, void *stream, void *const *events)
+{
+    g_err[0] = 0;
+    if (events == nullptr)
+        return fail(DSA_EINVAL, "events is NULL");
+    for (int i = 0; i < 10; i++)
+        if (events[i] == nullptr)
+            return fail(DSA_EINVAL, "events[%d] is NULL", i);
+    return decode_k_impl(shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_lens, kv_scale,
+                         sm_scale, scores, sel, out, ws, ws_bytes, stream,
+                         (hipEvent_t const *)events);
 }
 
 int dsa_decode_k_noalloc(const dsa_shape *shape, const void *q_idx, const float *w,

@@ -2,6 +2,7 @@
 // libdsa; the public interface is include/dsa.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -59,16 +60,25 @@ struct Workspace {
 };
 Workspace workspace_layout(const LaunchShape &ls);
 
+// Start and stop events bound to one kernel's dispatch: hipExtLaunchKernel
+// stamps them with that dispatch's own begin and end, so their span is the
+// kernel's run alone. Both null: an untimed launch.
+struct KTimer {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // gm4 / gm32 null: scores only. Otherwise the pass also writes the group
 // maxima the selection threshold is taken from.
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream);
+                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t = {});
 // have_group_max: the group maxima in the workspace were written by the
 // index pass of the same call; otherwise the selection computes them first.
+// t_filter / t_finish time the filter and the finish kernels.
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
-                  hipStream_t stream);
+                  hipStream_t stream, KTimer t_filter = {}, KTimer t_finish = {});
 // Pooled selection of pool_scores [R][score_stride(ls_pool)] over per-row
 // pool counts L_r / kp, expanded to token ids in sel [R][top_k * kp + kp - 1].
 // ls_pool is the token shape with max_len = max(1, max_len / kp); pool counts
@@ -82,9 +92,13 @@ int launch_cache_write(const LaunchShape &ls, const uint16_t *kv_a, const uint16
                        const uint16_t *k_proj, const uint16_t *k_w, const uint16_t *k_b,
                        const int32_t *seq_lens, const int32_t *block_tables, float eps,
                        float kv_scale, uint8_t *kv_cache, uint16_t *k_normed, hipStream_t stream);
+// t_att / t_merge time the attention and the merge kernels; with a single
+// chunk there is no merge and t_merge's events, if any, are recorded right
+// after the attention (a span of about zero).
 int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
                       float kv_scale, float sm_scale, uint16_t *out, char *ws,
-                      const Workspace &wl, hipStream_t stream);
+                      const Workspace &wl, hipStream_t stream, KTimer t_att = {},
+                      KTimer t_merge = {});
 
 } // namespace dsa

@@ -312,9 +312,10 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 template <int D, bool ONE_ROW, bool GM>
 static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
                        const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                       uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
+                       uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t)
 {
-    hipLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM>), grid, dim3(kIdxThreads), 0, stream,
+    hipExtLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM>), grid, dim3(kIdxThreads), 0, stream,
+                          t.start, t.stop, 0u,
                        q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.num_seqs,
                        ls.rows_per_seq,
                        ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls));
@@ -323,27 +324,27 @@ static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, 
 template <int D>
 static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
                      const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                     uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
+                     uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t)
 {
     const bool one = ls.rows_per_seq == 1;
     const bool gm = gm4 != nullptr;
     if (one && gm)
         launch_one<D, true, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
-                                  stream);
+                                  stream, t);
     else if (one)
         launch_one<D, true, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
-                                   stream);
+                                   stream, t);
     else if (gm)
         launch_one<D, false, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
-                                   stream);
+                                   stream, t);
     else
         launch_one<D, false, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
-                                    stream);
+                                    stream, t);
 }
 
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
-                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream)
+                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t)
 {
     // About kIdxWgTarget workgroups in all, balanced over the sequences by
     // their device-side lengths; each walks every W-th tile of one sequence
@@ -352,9 +353,9 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
         return -1;
     dim3 grid(kIdxWgTarget + ls.num_seqs); // enough for any split of the tiles
     if (ls.index_dim == 128)
-        launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream);
+        launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream, t);
     else if (ls.index_dim == 64)
-        launch_d<64>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream);
+        launch_d<64>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream, t);
     else
         return -1;
     return hipGetLastError() == hipSuccess ? 0 : -1;

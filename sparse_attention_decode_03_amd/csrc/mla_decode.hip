@@ -525,7 +525,7 @@ static int device_cus()
 int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *kv_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, const int32_t *sel,
                       float kv_scale, float sm_scale, uint16_t *out, char *ws,
-                      const Workspace &wl, hipStream_t stream)
+                      const Workspace &wl, hipStream_t stream, KTimer t_att, KTimer t_merge)
 {
     const int nch_max = att_chunks(ls) > 0 ? att_chunks(ls) : 1;
     const float qk_log2 = (float)((double)sm_scale * (double)kv_scale * 1.4426950408889634074);
@@ -545,18 +545,22 @@ int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *k
     const int hgc = (ls.num_heads + G - 1) / G;
     const dim3 grid(nch_max * hgc, ls.num_rows);
     auto kern = G == 16 ? k_mla_decode<16> : G == 32 ? k_mla_decode<32> : k_mla_decode<kAttHeads>;
-    hipLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, q, kv_cache, block_tables,
-                       seq_lens, sel, part_o, part_ml, out, ls.rows_per_seq, ls.num_heads,
-                       ls.top_k, ls.page_size, ls.max_blocks, ls.num_pages, ls.max_len, kv_scale,
-                       qk_log2, nch_max, hgc);
+    hipExtLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, t_att.start, t_att.stop, 0u, q,
+                          kv_cache, block_tables, seq_lens, sel, part_o, part_ml, out,
+                          ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size, ls.max_blocks,
+                          ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max, hgc);
     if (hipGetLastError() != hipSuccess)
         return -1;
     if (nch_max > 1) {
-        hipLaunchKernelGGL(k_mla_merge, dim3(ls.num_heads, ls.num_rows), dim3(128), 0, stream,
-                           part_o, part_ml, seq_lens, out, ls.num_heads, ls.top_k, ls.max_len,
-                           nch_max, hgc, G, kv_scale);
+        hipExtLaunchKernelGGL(k_mla_merge, dim3(ls.num_heads, ls.num_rows), dim3(128), 0, stream,
+                              t_merge.start, t_merge.stop, 0u, part_o, part_ml, seq_lens, out,
+                              ls.num_heads, ls.top_k, ls.max_len, nch_max, hgc, G, kv_scale);
         if (hipGetLastError() != hipSuccess)
             return -1;
+    } else {
+        for (hipEvent_t e : {t_merge.start, t_merge.stop})
+            if (e != nullptr && hipEventRecord(e, stream) != hipSuccess)
+                return -1;
     }
     return 0;
 }

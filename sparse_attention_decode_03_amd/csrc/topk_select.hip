@@ -836,7 +836,7 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
 
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
-                  hipStream_t stream)
+                  hipStream_t stream, KTimer t_filter, KTimer t_finish)
 {
     const int pmax = sel_slices(ls);
     const int stride = score_stride(ls);
@@ -848,11 +848,12 @@ int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq
     if (!have_group_max)
         hipLaunchKernelGGL(k_group_max, slices, dim3(kSliceThreads), 0, stream, scores, seq_lens,
                            gm4, gm32, ls.max_len, stride);
-    hipLaunchKernelGGL(k_select_filter, slices, dim3(kSliceThreads), 0, stream, scores, seq_lens,
-                       gm4, gm32, cand, cnt, ls.max_len, stride, ls.top_k, pmax);
-    hipLaunchKernelGGL(k_select_finish, dim3(ls.num_rows), dim3(kFinThreads), 0, stream, scores,
-                       seq_lens, cand, cnt, sel, (uint32_t *)(ws + wl.bitmap), ls.max_len, stride,
-                       ls.top_k, pmax);
+    hipExtLaunchKernelGGL(k_select_filter, slices, dim3(kSliceThreads), 0, stream, t_filter.start,
+                          t_filter.stop, 0u, scores, seq_lens, gm4, gm32, cand, cnt, ls.max_len,
+                          stride, ls.top_k, pmax);
+    hipExtLaunchKernelGGL(k_select_finish, dim3(ls.num_rows), dim3(kFinThreads), 0, stream,
+                          t_finish.start, t_finish.stop, 0u, scores, seq_lens, cand, cnt, sel,
+                          (uint32_t *)(ws + wl.bitmap), ls.max_len, stride, ls.top_k, pmax);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

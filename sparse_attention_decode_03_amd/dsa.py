@@ -34,6 +34,7 @@ EXPORTS = (
     "dsa_mla_decode",
     "dsa_decode_k",
     "dsa_decode_k_noalloc",
+    "dsa_decode_k_timed",
     "dsa_cache_write",
     "dsa_topk_select_pooled",
     "dsa_pooled_workspace_bytes",
@@ -114,6 +115,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_mla_decode.restype = i32
     lib.dsa_decode_k.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P, sz, P]
     lib.dsa_decode_k.restype = i32
+    lib.dsa_decode_k_timed.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P, sz, P,
+                                       ctypes.POINTER(ctypes.c_void_p)]
+    lib.dsa_decode_k_timed.restype = i32
     lib.dsa_decode_k_noalloc.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P]
     lib.dsa_decode_k_noalloc.restype = i32
     lib.dsa_cache_write.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P]
@@ -237,6 +241,22 @@ def check_metadata(shape: Shape, seq_lens, block_tables, sel=None, stream=None) 
         return
     _check(load().dsa_check_metadata(ctypes.byref(shape), _ptr(seq_lens), _ptr(block_tables),
                                      _ptr(sel), DSA_META_DEVICE, _stream(stream)))
+
+
+def decode_k_timed(shape: Shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_lens,
+                   kv_scale: float, sm_scale: float, scores, sel, out, ws, events,
+                   ws_bytes: Optional[int] = None, stream=None) -> None:
+    """dsa_decode_k with ten torch.cuda.Events (timing enabled, each already
+    recorded once so that it exists) bound in start/stop pairs to the index,
+    filter, finish, attention and merge kernels."""
+    if len(events) != 10:
+        raise ValueError("decode_k_timed takes 10 events")
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    handles = (ctypes.c_void_p * 10)(*[e.cuda_event for e in events])
+    _check(load().dsa_decode_k_timed(ctypes.byref(shape), _ptr(q_idx), _ptr(w), _ptr(k_normed),
+                                     _ptr(q), _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens),
+                                     kv_scale, sm_scale, _ptr(scores), _ptr(sel), _ptr(out),
+                                     _ptr(ws), nb, _stream(stream), handles))
 
 
 def decode_k_noalloc(shape: Shape, q_idx, w, k_normed, q, kv_cache, block_tables, seq_lens,

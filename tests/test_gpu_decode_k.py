@@ -90,3 +90,30 @@ def test_verify_workload_at_full_size_is_bit_identical_to_serial_calls():
     must agree."""
     inputs = wl.make_inputs(wl.WORKLOADS["kverify"])
     assert_serial_equals_batched(inputs)
+
+
+def test_timed_entry_point_writes_the_same_bytes():
+    # dsa_decode_k_timed launches the same kernels as dsa_decode_k with a
+    # start/stop HIP event pair bound to each: its outputs must match byte
+    # for byte, every pair must span a non-negative time, and the pairs must
+    # follow the stream order.
+    inputs = small(num_seqs=2, rows_per_seq=4, lengths="verify", base=5000, top_k=2048, seed=77)
+    a = dsa.DeviceStep(inputs)
+    a.decode_k()
+    b = dsa.DeviceStep(inputs)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+    for e in evs:
+        e.record(stream)
+    torch.cuda.synchronize()
+    dsa.decode_k_timed(b.shape, b.q_idx, b.w, b.k_normed, b.q, b.kv_cache, b.block_tables,
+                       b.seq_lens, b.kv_scale, b.sm_scale, b.scores, b.sel, b.out, b.ws, evs,
+                       stream=stream)
+    torch.cuda.synchronize()
+    assert torch.equal(a.sel, b.sel)
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    spans = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(5)]
+    assert all(s >= 0.0 for s in spans), spans
+    assert spans[0] > 0.0 and spans[3] > 0.0, spans
+    gaps = [evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(4)]
+    assert all(g >= 0.0 for g in gaps), gaps
