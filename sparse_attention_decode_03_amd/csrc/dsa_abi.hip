@@ -48,8 +48,9 @@ int check_shape(const dsa_shape *sh, dsa::LaunchShape *ls)
         sh->index_heads < 1 || sh->index_dim < 1 || sh->top_k < 1 || sh->page_size < 1 ||
         sh->max_len < 1 || sh->k_capacity < 1 || sh->max_blocks_per_seq < 1 || sh->num_pages < 1)
         return fail(DSA_EINVAL, "every dsa_shape field must be positive");
-    if (sh->rows_per_seq > 16)
-        return fail(DSA_EUNSUPPORTED, "rows_per_seq %d outside [1, 16]", sh->rows_per_seq);
+    if (sh->rows_per_seq > dsa::kMaxRowsPerSeq)
+        return fail(DSA_EUNSUPPORTED, "rows_per_seq %d outside [1, %d]", sh->rows_per_seq,
+                    dsa::kMaxRowsPerSeq);
     if (sh->latent_dim != 512)
         return fail(DSA_EUNSUPPORTED, "latent_dim %d: only 512 is supported", sh->latent_dim);
     if (sh->num_heads > 128)

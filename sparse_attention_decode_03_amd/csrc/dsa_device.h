@@ -12,6 +12,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer resource on gfx9-family chips: 32-bit data format,
+// no swizzle, no stride; with stride 0 the range check compares the byte
+// offset with the record count, and a load past it returns zeros.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of the buffer load builtins: the non-temporal bit.
+constexpr int kCachePolicyNT = 2;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;

@@ -39,6 +39,10 @@ inline int score_stride(const LaunchShape &ls) { return (ls.max_len + 63) / 64 *
 // Index-score pass geometry: 256-token tiles (the balance of tiles over
 // workgroups is computed on the device from the lengths).
 constexpr int kIdxTile = 256;
+// A last tile this short does not count as a tile of work in the split.
+constexpr int kIdxLightTail = 32;
+// Rows per sequence the boundary accepts (K of a verify or row group).
+constexpr int kMaxRowsPerSeq = 16;
 
 inline int att_chunks(const LaunchShape &ls)
 {

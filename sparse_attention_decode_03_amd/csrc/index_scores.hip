@@ -37,6 +37,44 @@ constexpr int kIdxWgTarget = 512; // workgroups the tiles of a call spread over
 
 // LDS: the key tile, 256 tokens x 16 chunks of 16 bytes (64 KiB at D = 128).
 
+// The epilogue of one 32-token block of one row from its 32x32 MFMA result
+// (lane: token t, 16 head partials): ReLU-weighted head sum, the score store
+// and (GM) the group maxima. srow, g4row and g32row point at the row's
+// scores and group-maximum rows; t is the lane's token, L the row length.
+template <bool GM>
+__device__ __forceinline__ void block_epilogue(const float (&wv)[16], const floatx16 &acc, int lane,
+                                               int t, int L, float *srow, uint32_t *g4row,
+                                               uint32_t *g32row)
+{
+    // ReLU as a signed-integer max on the bits: a negative float (sign bit
+    // set) compares below 0, so this is max(x, 0) for every non-NaN x (-0
+    // gives +0) in one instruction; fmaxf would first quiet a possible
+    // signalling NaN with an extra instruction per value
+    float part = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; v++)
+        part = __builtin_fmaf(wv[v], __int_as_float(max(__float_as_int(acc[v]), 0)), part);
+    const float tot = add_xor32(part);
+    const int hl = lane / 32;
+    if (hl == 0 && t < L)
+        srow[t] = tot;
+    if (GM) {
+        // groups are aligned: a quad of lanes holds a 4-token group, lanes
+        // 0..31 the 32-token group
+        uint32_t k = t < L ? score_key(tot) : 0u;
+        k = max(k, dpp_u32<kDppQuadXor1>(k));
+        k = max(k, dpp_u32<kDppQuadXor2>(k));
+        if (hl == 0 && (lane & 3) == 0 && t < L)
+            g4row[t >> 2] = k;
+        k = max(k, dpp_u32<kDppRowHalfMirror>(k));
+        k = max(k, dpp_u32<kDppRowMirror>(k)); // every lane: its row's max
+        const uint32_t k32 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 0),
+                                 (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
+        if (lane == 0 && t < L)
+            g32row[t >> 5] = k32;
+    }
+}
+
 template <int D, bool ONE_ROW, bool GM>
 __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
@@ -51,7 +89,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave); // uniform: scalar row math
     const int hl = lane / 32;
 
     // ---- balance the tiles of all sequences over about kIdxWgTarget
@@ -60,26 +98,45 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     // ceil(tiles_s / tpw) workgroups, and this workgroup claims its sequence
     // and slot from a prefix of those counts ----
     __shared__ uint32_t bscan[kIdxThreads / kWave + 1];
-    __shared__ int claim[3];
-    auto seq_tiles = [&](int sq) {
+    __shared__ int claim[4];
+    __shared__ int s_len[kMaxRowsPerSeq]; // lengths of the claimed sequence's rows
+    auto row_len = [&](int r) { return min(max(seq_lens[r], 0), max_len); };
+    auto seq_lmax = [&](int sq) {
         int lm = 0;
         for (int j = 0; j < K; j++)
-            lm = max(lm, min(max(seq_lens[sq * K + j], 0), max_len));
-        return (lm + kIdxTile - 1) / kIdxTile;
+            lm = max(lm, row_len(sq * K + j));
+        return lm;
     };
     const int per = (S + kIdxThreads - 1) / kIdxThreads; // sequences per thread
     const int sq0 = min(tid * per, S), sq1 = min(sq0 + per, S);
+    // the first sequence's length is kept (the only one up to 256 sequences)
+    const int lm0 = sq0 < sq1 ? seq_lmax(sq0) : 0;
+    // Tiles that count for the split: a last tile of at most kIdxLightTail
+    // tokens costs about one 32-token block and rides along with another
+    // tile's workgroup (the interleave below hands it to one of them).
+    auto tiles_of = [&](int lm) {
+        const int nt = (lm + kIdxTile - 1) / kIdxTile;
+        return (uint32_t)(nt > 1 && lm - (nt - 1) * kIdxTile <= kIdxLightTail ? nt - 1 : nt);
+    };
     uint32_t my_tiles = 0;
     for (int sq = sq0; sq < sq1; sq++)
-        my_tiles += (uint32_t)seq_tiles(sq);
+        my_tiles += tiles_of(sq == sq0 ? lm0 : seq_lmax(sq));
     uint32_t total_tiles;
     (void)block_exclusive_scan<kIdxThreads>(my_tiles, bscan, &total_tiles);
-    const uint32_t tpw = max(1u, (total_tiles + kIdxWgTarget - 1) / kIdxWgTarget);
-    uint32_t my_wgs = 0;
-    for (int sq = sq0; sq < sq1; sq++)
-        my_wgs += ((uint32_t)seq_tiles(sq) + tpw - 1) / tpw;
-    uint32_t total_wgs;
-    uint32_t wg_base = block_exclusive_scan<kIdxThreads>(my_wgs, bscan, &total_wgs);
+    // Tiles per workgroup: the smallest count from ceil(total / target) up
+    // whose split needs at most kIdxWgTarget workgroups (two per CU, all
+    // resident at once), tried a few times; any count from the first on
+    // needs at most kIdxWgTarget + S workgroups, the grid.
+    uint32_t tpw = max(1u, (total_tiles + kIdxWgTarget - 1) / kIdxWgTarget);
+    uint32_t my_wgs, wg_base, total_wgs;
+    for (int attempt = 0;; attempt++, tpw++) {
+        my_wgs = 0;
+        for (int sq = sq0; sq < sq1; sq++)
+            my_wgs += (tiles_of(sq == sq0 ? lm0 : seq_lmax(sq)) + tpw - 1) / tpw;
+        wg_base = block_exclusive_scan<kIdxThreads>(my_wgs, bscan, &total_wgs);
+        if (total_wgs <= (uint32_t)kIdxWgTarget || attempt == 3)
+            break;
+    }
     if (tid == 0)
         claim[0] = -1;
     __syncthreads();
@@ -87,12 +144,15 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     if (me >= wg_base && me < wg_base + my_wgs) { // exactly one thread
         uint32_t at = wg_base;
         for (int sq = sq0; sq < sq1; sq++) {
-            const int nt = seq_tiles(sq);
-            const uint32_t w_s = ((uint32_t)nt + tpw - 1) / tpw;
+            const int lm = sq == sq0 ? lm0 : seq_lmax(sq);
+            const uint32_t w_s = (tiles_of(lm) + tpw - 1) / tpw;
             if (me < at + w_s) {
                 claim[0] = sq;
                 claim[1] = (int)(me - at);
                 claim[2] = (int)w_s;
+                claim[3] = lm;
+                for (int j = 0; j < K; j++)
+                    s_len[j] = row_len(sq * K + j);
                 break;
             }
             at += w_s;
@@ -102,10 +162,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     if (claim[0] < 0)
         return; // past the last workgroup this split needs
     const int s = claim[0];
-
-    int lmax = 0;
-    for (int j = 0; j < K; j++)
-        lmax = max(lmax, min(max(seq_lens[s * K + j], 0), max_len));
+    // the longest row of the sequence: the tiles to score (from the claim, so
+    // the first tile's loads go out with no further length load)
+    const int lmax = claim[3];
     // tiles interleave across the sequence's workgroups (workgroup x takes
     // tiles x, x + W, x + 2W, ...), so at any moment the workgroups stream
     // neighbouring 64 KiB blocks and spread over every HBM channel
@@ -115,23 +174,22 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     if (tile_first >= tile_end)
         return;
 
-    const uint16_t *kseq = k_normed + (int64_t)s * cap * D;
+    // The sequence's keys as a buffer resource whose range ends at the
+    // longest row: the hardware returns zeros for loads past it, so the key
+    // loads need no mask and no 64-bit address arithmetic. The whole offset
+    // goes in the per-lane operand, the one the range check tests.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(k_normed + (int64_t)s * cap * D), 0, lmax * D * 2, kBufferWord3);
     u32x4 regs[LOADS];
-    // loads [I0, I1) of a tile's share of this thread
+    // loads [I0, I1) of a tile's share of this thread: 16-byte piece
+    // i * kIdxThreads + tid of the tile, i.e. row g / CH, chunk g % CH
     auto load_part = [&](int tile, auto i0c, auto i1c) {
         constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
-        const int t0 = tile * kIdxTile;
+        const int tile_bytes = tile * kIdxTile * D * 2;
 #pragma unroll
-        for (int i = I0; i < I1; i++) {
-            const int g = i * kIdxThreads + tid;
-            const int row = g / CH;
-            const int c = g % CH;
-            if (t0 + row < lmax)
-                regs[i] = __builtin_nontemporal_load(
-                    (const u32x4 *)(kseq + (int64_t)(t0 + row) * D + c * 8));
-            else
-                regs[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = I0; i < I1; i++)
+            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, tile_bytes + (i * kIdxThreads + tid) * 16,
+                                                            0, kCachePolicyNT);
     };
     using IC0 = std::integral_constant<int, 0>;
     using ICH = std::integral_constant<int, LOADS / 2>;
@@ -171,35 +229,12 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
             wv[v] = (h < Hi) ? x : 0.0f;
         }
     };
-    if (ONE_ROW)
-        load_row(s);
 
-    // The epilogue of one 32-token block of row r from its MFMA result:
-    // ReLU-weighted head sum, the score store and (GM) the group maxima.
+    // The epilogue of one 32-token block of row r.
     auto block_out = [&](int r, int L, int t0, int col0, const floatx16 &acc) {
-        float part = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; v++)
-            part = __builtin_fmaf(wv[v], __builtin_fmaxf(acc[v], 0.0f), part);
-        const float tot = add_xor32(part);
-        const int t = t0 + col0 + (lane & 31);
-        if (hl == 0 && t < L)
-            scores[(int64_t)r * stride + t] = tot;
-        if (GM) {
-            // groups are aligned: a quad of lanes holds a 4-token group,
-            // lanes 0..31 the 32-token group
-            uint32_t k = t < L ? score_key(tot) : 0u;
-            k = max(k, dpp_u32<kDppQuadXor1>(k));
-            k = max(k, dpp_u32<kDppQuadXor2>(k));
-            if (hl == 0 && (lane & 3) == 0 && t < L)
-                gm4[(int64_t)r * (stride / 4) + (t >> 2)] = k;
-            k = max(k, dpp_u32<kDppRowHalfMirror>(k));
-            k = max(k, dpp_u32<kDppRowMirror>(k)); // every lane: its row's max
-            const uint32_t k32 = max((uint32_t)__builtin_amdgcn_readlane((int)k, 0),
-                                     (uint32_t)__builtin_amdgcn_readlane((int)k, 16));
-            if (lane == 0 && t < L)
-                gm32[(int64_t)r * (stride / 32) + (t >> 5)] = k32;
-        }
+        block_epilogue<GM>(wv, acc, lane, t0 + col0 + (lane & 31), L, scores + (int64_t)r * stride,
+                           GM ? gm4 + (int64_t)r * (stride / 4) : nullptr,
+                           GM ? gm32 + (int64_t)r * (stride / 32) : nullptr);
     };
     // One 32-token block: MFMA over D, then the epilogue.
     auto score_block = [&](int r, int L, int t0, int col0, const bf16x8 (&kb)[KS]) {
@@ -248,13 +283,17 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     constexpr int kBlocks = kIdxTile / 32;
     const int items = K * kBlocks / (kIdxThreads / kWave);
     const int item0 = wave * items;
+    // The first tile's key loads go out before the query's: the query is
+    // used (padding heads zeroed) as soon as it lands, and loads issued
+    // after it would wait for it.
+    load_part(tile_first, IC0{}, ICL{});
     int loaded = -1;
-    if (!ONE_ROW && item0 / kBlocks == (item0 + items - 1) / kBlocks) {
+    if (ONE_ROW) {
+        load_row(s);
+    } else if (item0 / kBlocks == (item0 + items - 1) / kBlocks) {
         loaded = item0 / kBlocks;
         load_row(s * K + loaded);
     }
-
-    load_part(tile_first, IC0{}, ICL{});
     for (int tile = tile_first; tile < tile_end; tile += W) {
         const int t0 = tile * kIdxTile;
         const bool more = tile + W < tile_end;
@@ -282,10 +321,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                     kb[b][ks] = as_bf16x8(lds[row * CH + (c ^ (row & (CH - 1)))]);
                 }
             }
-            const int L = min(max(seq_lens[s], 0), max_len);
 #pragma unroll
             for (int b = 0; b < 2; b++)
-                score_block(s, L, t0, wave * 64 + b * 32, kb[b]);
+                score_block(s, lmax, t0, wave * 64 + b * 32, kb[b]);
         } else {
             // the wave's (row, 32-token block) items, two at a time: a range
             // starts at an even item and the blocks per row are even, so a
@@ -296,7 +334,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                 const int j = it / kBlocks;
                 const int blk = it % kBlocks;
                 const int r = s * K + j;
-                const int L = min(max(seq_lens[r], 0), max_len);
+                const int L = s_len[j]; // from LDS: no wait on the loads in flight
                 if (t0 + blk * 32 >= L)
                     continue;
                 if (j != loaded) {
@@ -346,11 +384,11 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
                         uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t)
 {
+    if ((gm4 == nullptr) != (gm32 == nullptr))
+        return -1;
     // About kIdxWgTarget workgroups in all, balanced over the sequences by
     // their device-side lengths; each walks every W-th tile of one sequence
     // with the next tile's loads in flight.
-    if ((gm4 == nullptr) != (gm32 == nullptr))
-        return -1;
     dim3 grid(kIdxWgTarget + ls.num_seqs); // enough for any split of the tiles
     if (ls.index_dim == 128)
         launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream, t);
