@@ -85,20 +85,21 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(v2i w)
 }
 
 // Folding the per-chunk partials of one (row, head) at latent columns
-// d .. d + 3, strictly in chunk order 0, 1, 2, ... with one fp32 formula.
+// d .. d + 7, strictly in chunk order 0, 1, 2, ... with one fp32 formula.
 // Partials are loaded in unrolled batches (independent loads in flight), then
 // folded; straight-line code with selects, so the batch stays in registers. A
 // batch is the chunk count of a row at top_k = 2048 (8 x 256 slots): a larger
 // one re-reads the last chunk (measured: 16 cost 3.5 us per step at
 // 64 x 16.4k).
 constexpr int kFoldBatch = 8;
+constexpr int kFoldCols = 8; // latent columns per lane (16 bytes of bf16)
 struct FoldState {
     float m, l;
-    floatx4 acc;
+    float acc[kFoldCols];
 };
 struct FoldBatch {
     float2 ml[kFoldBatch];
-    floatx4 ov[kFoldBatch];
+    u32x4 ov[kFoldBatch];
 };
 // chunks past `last` re-read it (branch-free; they are not folded)
 __device__ __forceinline__ void fold_load(const uint16_t *part_o, const float2 *part_ml, int64_t pbase,
@@ -108,9 +109,7 @@ __device__ __forceinline__ void fold_load(const uint16_t *part_o, const float2 *
     for (int k = 0; k < kFoldBatch; k++) {
         const int64_t pi = pbase + (int64_t)min(c0 + k, last) * G;
         b.ml[k] = part_ml[pi];
-        const u32x2 pk = *(const u32x2 *)(part_o + pi * kLat + d);
-        b.ov[k] = floatx4{__uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u),
-                          __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)};
+        b.ov[k] = *(const u32x4 *)(part_o + pi * kLat + d);
     }
 }
 __device__ __forceinline__ void fold_step(int c0, int nch, const FoldBatch &b, FoldState &f)
@@ -125,17 +124,21 @@ __device__ __forceinline__ void fold_step(int c0, int nch, const FoldBatch &b, F
         const float e = use ? exp2f(b.ml[k].x - m_new) : 0.0f;
         f.l = use ? __builtin_fmaf(b.ml[k].y, e, f.l * a) : f.l;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            f.acc[i] = use ? __builtin_fmaf(b.ov[k][i], e, f.acc[i] * a) : f.acc[i];
+        for (int i = 0; i < kFoldCols; i++) {
+            const uint32_t w = b.ov[k][i / 2];
+            const float o = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            f.acc[i] = use ? __builtin_fmaf(o, e, f.acc[i] * a) : f.acc[i];
+        }
         f.m = use ? m_new : f.m;
     }
 }
-__device__ __forceinline__ u32x2 fold_output(const FoldState &f, float kv_scale)
+__device__ __forceinline__ u32x4 fold_output(const FoldState &f, float kv_scale)
 {
     const float inv = f.l > 0.0f ? kv_scale / f.l : 0.0f;
-    u32x2 packed;
-    packed.x = pack_bf16x2(f.acc[0] * inv, f.acc[1] * inv);
-    packed.y = pack_bf16x2(f.acc[2] * inv, f.acc[3] * inv);
+    u32x4 packed;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        packed[i] = pack_bf16x2(f.acc[2 * i] * inv, f.acc[2 * i + 1] * inv);
     return packed;
 }
 
@@ -438,7 +441,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 
     // Output through LDS: the waves park O (G heads x 512 columns, bf16) in
     // the idle ring, then write it back as whole 1 KiB head rows with 16-byte
-    // stores (measured faster than 8-byte stores straight from registers).
+    // stores (measured faster than 8-byte stores straight from registers,
+    // with 16 heads as with 64).
     constexpr int kORowBytes = 2 * kLat + 16; // padded: 16 rows at one column spread over the banks
     static_assert(G * kORowBytes <= (int)sizeof(ring), "O fits the ring");
 #pragma unroll
@@ -472,22 +476,27 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     }
 }
 
-// Fold the per-chunk partials of every (row, head).
+// Fold the per-chunk partials of every (row, head): one wave per head,
+// kMergeHeads heads per workgroup, 8 latent columns per lane (the (m, l)
+// pairs of a head are wave-uniform loads).
 // The partial pointers carry no __restrict__, so the first batch's loads are
 // not sunk below the row-length test: loads through const restrict pointers
 // count as invariant and move freely.
-__global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *part_o,
-                                                   const float2 *part_ml,
-                                                   const int32_t *__restrict__ seq_lens,
-                                                   uint16_t *__restrict__ out, int H, int top_k,
-                                                   int max_len, int nch_max, int hg_count,
-                                                   int G, float kv_scale)
+constexpr int kMergeHeads = 4;
+__global__ __launch_bounds__(kWave * kMergeHeads) void k_mla_merge(const uint16_t *part_o,
+                                                                  const float2 *part_ml,
+                                                                  const int32_t *__restrict__ seq_lens,
+                                                                  uint16_t *__restrict__ out, int H,
+                                                                  int top_k, int max_len, int nch_max,
+                                                                  int hg_count, int G, float kv_scale)
 {
     const int r = blockIdx.y;
-    const int h = blockIdx.x;
+    const int h = blockIdx.x * kMergeHeads + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (h >= H)
+        return;
     const int hg = h / G;
     const int hl = h % G;
-    const int d = threadIdx.x * 4;
+    const int d = (threadIdx.x % kWave) * kFoldCols;
     const int64_t pbase = ((int64_t)r * hg_count + hg) * nch_max * G + hl;
     FoldBatch b;
     // the first batch goes out before the row's chunk count is known (every
@@ -499,13 +508,18 @@ __global__ __launch_bounds__(128) void k_mla_merge(const uint16_t *part_o,
     const int nch = (n + kAttChunk - 1) / kAttChunk;
     if (nch <= 1)
         return;
-    FoldState f{kNegInf, 0.0f, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+    FoldState f;
+    f.m = kNegInf;
+    f.l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kFoldCols; i++)
+        f.acc[i] = 0.0f;
     for (int c0 = 0; c0 < nch; c0 += kFoldBatch) {
         if (c0 > 0)
             fold_load(part_o, part_ml, pbase, G, c0, nch - 1, d, b);
         fold_step(c0, nch, b, f);
     }
-    *(u32x2 *)(out + ((int64_t)r * H + h) * kLat + d) = fold_output(f, kv_scale);
+    *(u32x4 *)(out + ((int64_t)r * H + h) * kLat + d) = fold_output(f, kv_scale);
 }
 
 // Compute units of the current device (cached per device).
@@ -555,7 +569,8 @@ int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *k
     if (hipGetLastError() != hipSuccess)
         return -1;
     if (nch_max > 1) {
-        hipExtLaunchKernelGGL(k_mla_merge, dim3(ls.num_heads, ls.num_rows), dim3(128), 0, stream,
+        hipExtLaunchKernelGGL(k_mla_merge, dim3((ls.num_heads + kMergeHeads - 1) / kMergeHeads, ls.num_rows),
+                              dim3(kWave * kMergeHeads), 0, stream,
                               t_merge.start, t_merge.stop, 0u, part_o, part_ml, seq_lens, out,
                               ls.num_heads, ls.top_k, ls.max_len, nch_max, hgc, G, kv_scale);
         if (hipGetLastError() != hipSuccess)
