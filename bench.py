@@ -271,6 +271,12 @@ def main() -> int:
         stage_mean_us = {nm: float(np.mean([sev[i][2 * j].elapsed_time(sev[i][2 * j + 1]) * 1e3
                                             for i in range(nst)]))
                          for j, nm in enumerate(stage_names)}
+        # stages that launch no kernel for this shape (their events are
+        # recorded back to back: the span is no kernel's)
+        if int(inputs["max_len"]) <= dsa.SELECT_DIRECT_MAX:
+            stage_us["select_filter"] = None  # the selection is one kernel (select_finish)
+        if min(int(inputs["top_k"]), int(inputs["max_len"])) <= 256:
+            stage_us["merge"] = None  # one attention chunk per row: no merge
 
         # dominant kernel, standalone: the index-score pass launched back to
         # back on rotating replicas between one pair of HIP events (a
@@ -295,7 +301,7 @@ def main() -> int:
     # the indexer plus the gather-attend (attention and chunk merge), against
     # every algorithmic byte of the step (keys, selected rows, q/out,
     # q_idx/w, block-table entries)
-    ia_us = stage_us["index"] + stage_us["attend"] + stage_us["merge"]
+    ia_us = stage_us["index"] + stage_us["attend"] + (stage_us["merge"] or 0.0)
     ia_gbs = ab["total"] / (ia_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,

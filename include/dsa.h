@@ -140,7 +140,11 @@ int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
  *   sel      [R, top_k] int32 (output): the n_r selected ids in ascending
  *            order, then -1 in every slot past n_r
  *   ws       workspace of at least dsa_workspace_bytes(shape) bytes
+ * With max_len at most DSA_SELECT_DIRECT_MAX the selection is one kernel
+ * that holds whole rows; longer rows take a threshold filter and a finish
+ * (two kernels). The result is the same unique top-k either way.
  */
+#define DSA_SELECT_DIRECT_MAX 8192
 int dsa_topk_select(const dsa_shape *shape, const float *scores, const int32_t *seq_lens,
                     int32_t *sel, void *ws, size_t ws_bytes, void *stream);
 
@@ -195,10 +199,13 @@ int dsa_decode_k(const dsa_shape *shape, const void *q_idx, const float *w,
  * launched with hipExtLaunchKernel and a start/stop pair of caller-created
  * HIP events (hipEvent_t, created with timing), so that the span of a pair
  * is that kernel's own run. events[0..9] are the pairs of the index pass,
- * the selection's filter, its finish, the attention and the chunk merge;
- * when no row has more than one chunk there is no merge and its two events
- * are recorded right after the attention. Results are those of
- * dsa_decode_k. Refusals as dsa_decode_k, and DSA_EINVAL for a NULL event.
+ * the selection's filter, its finish, the attention and the chunk merge.
+ * A stage without a kernel has its two events recorded back to back in
+ * stream order (their span is no kernel's): the merge when no row has more
+ * than one chunk, the filter when the selection is one kernel (max_len at
+ * most DSA_SELECT_DIRECT_MAX; the finish's pair then times that kernel).
+ * Results are those of dsa_decode_k. Refusals as dsa_decode_k, and
+ * DSA_EINVAL for a NULL event.
  */
 int dsa_decode_k_timed(const dsa_shape *shape, const void *q_idx, const float *w,
                        const void *k_normed, const void *q, const uint8_t *kv_cache,

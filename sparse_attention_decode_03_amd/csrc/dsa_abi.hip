@@ -145,6 +145,8 @@ int pooled_layout(const dsa_shape *shape, int32_t kp, PooledLayout *pl)
 
 } // namespace
 
+static_assert(DSA_SELECT_DIRECT_MAX == dsa::kSelDirectMax, "header and kernels agree");
+
 namespace dsa {
 
 Workspace workspace_layout(const LaunchShape &ls)
@@ -377,10 +379,13 @@ int decode_k_impl(const dsa_shape *shape, const void *q_idx, const float *w, con
         }
         return t;
     };
+    // the group maxima only feed the threshold filter of long rows
+    const bool gm = !dsa::select_direct(ls);
     if ((rc = launched(dsa::launch_index_scores(ls, (const uint16_t *)q_idx, w,
                                                 (const uint16_t *)k_normed, seq_lens, scores,
-                                                (uint32_t *)(wsb + wl.gm4),
-                                                (uint32_t *)(wsb + wl.gm32), st, timer(0)),
+                                                gm ? (uint32_t *)(wsb + wl.gm4) : nullptr,
+                                                gm ? (uint32_t *)(wsb + wl.gm32) : nullptr, st,
+                                                timer(0)),
                        "index_scores")) ||
         (rc = launched(dsa::launch_select(ls, scores, seq_lens, sel, wsb, wl, true, st, timer(1),
                                           timer(2)),

@@ -77,9 +77,19 @@ struct KTimer {
 int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const float *w,
                         const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
                         uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t = {});
+// Rows of at most kSelDirectMax tokens (by the shape's max_len) are
+// selected by one kernel that holds the whole row (no group maxima needed);
+// longer ones by the threshold filter and the finish.
+// (Measured: up to 8192 tokens one kernel wins, 22 us against 16 for the
+// two kernels at 64 rows x 16384; the whole-row histograms contend.)
+constexpr int kSelDirectMax = 8192;
+inline bool select_direct(const LaunchShape &ls) { return ls.max_len <= kSelDirectMax; }
 // have_group_max: the group maxima in the workspace were written by the
-// index pass of the same call; otherwise the selection computes them first.
-// t_filter / t_finish time the filter and the finish kernels.
+// index pass of the same call; otherwise the selection computes them first
+// (neither matters with select_direct).
+// t_filter / t_finish time the filter and the finish kernels (with
+// select_direct: the finish's pair times the one kernel, the filter's spans
+// nothing).
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
                   hipStream_t stream, KTimer t_filter = {}, KTimer t_finish = {});

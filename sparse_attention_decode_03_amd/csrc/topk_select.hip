@@ -834,6 +834,61 @@ __global__ __launch_bounds__(kFinThreads) void k_select_finish(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Direct: rows of at most kSelDirectMax tokens in one kernel. One workgroup
+// per row holds the whole row, thread t the tokens [t * RUN, t * RUN + RUN)
+// (ascending, thread-major, as the finish holds its candidates), and runs
+// the finish's exact cut on all of them: no threshold, no candidate lists,
+// no second kernel. The result is the same unique top-k.
+template <int RUN>
+__global__ __launch_bounds__(kFinThreads) void k_select_direct(const float *__restrict__ scores,
+                                                               const int32_t *__restrict__ seq_lens,
+                                                               int32_t *__restrict__ sel, int max_len,
+                                                               int stride, int top_k)
+{
+    static_assert(RUN % 4 == 0 && RUN <= 32, "float4 loads, one mask bit per token");
+    __shared__ __align__(16) uint8_t area[2 * kSelHistWords * 4 + kRankList * 8];
+    __shared__ BinSearch bs;
+    __shared__ uint32_t ccount;
+
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = row_len(seq_lens, r, max_len);
+    int32_t *out = sel + (int64_t)r * top_k;
+    if (L <= top_k) { // every token is selected; slots past L are padding
+        for (int slot = tid; slot < top_k; slot += kFinThreads)
+            out[slot] = slot < L ? slot : -1;
+        return;
+    }
+    const float *srow = scores + (int64_t)r * stride;
+    const int t0 = tid * RUN;
+    uint32_t kk[RUN], id[RUN];
+    floatx4 v[RUN / 4];
+#pragma unroll
+    for (int q = 0; q < RUN / 4; q++) // a load only where its first token is in the row
+        v[q] = (t0 + 4 * q < L) ? *(const floatx4 *)(srow + t0 + 4 * q)
+                                : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t valid = 0u, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int j = 0; j < RUN; j++) {
+        kk[j] = score_key(v[j / 4][j % 4]);
+        id[j] = (uint32_t)(t0 + j);
+        if (t0 + j < L) {
+            valid |= 1u << j;
+            lo = min(lo, kk[j]);
+            hi = max(hi, kk[j]);
+        }
+    }
+    for (int i = tid; i < 2 * kSelHistWords; i += kFinThreads)
+        ((uint32_t *)area)[i] = 0u;
+    if (tid == 0)
+        ccount = 0u;
+    block_minmax<kFinThreads>(lo, hi, &bs); // its barrier publishes the cleared bins
+    // every token of the row is a candidate, so the first window holds
+    // L > top_k of them and the cut never reports a shortfall
+    (void)exact_cut_write<RUN>(kk, id, valid, lo, hi, top_k, out, area, bs, ccount);
+}
+
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,
                   int32_t *sel, char *ws, const Workspace &wl, bool have_group_max,
                   hipStream_t stream, KTimer t_filter, KTimer t_finish)
@@ -844,6 +899,16 @@ int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq
     uint32_t *gm32 = (uint32_t *)(ws + wl.gm32);
     u32x2 *cand = (u32x2 *)(ws + wl.cand);
     uint32_t *cnt = (uint32_t *)(ws + wl.cnt);
+    if (select_direct(ls)) {
+        // one kernel; the filter's events, if any, span nothing
+        for (hipEvent_t e : {t_filter.start, t_filter.stop})
+            if (e != nullptr && hipEventRecord(e, stream) != hipSuccess)
+                return -1;
+        static_assert(kSelDirectMax <= 8 * kFinThreads, "eight tokens a thread");
+        hipExtLaunchKernelGGL(k_select_direct<8>, dim3(ls.num_rows), dim3(kFinThreads), 0, stream, t_finish.start,
+                              t_finish.stop, 0u, scores, seq_lens, sel, ls.max_len, stride, ls.top_k);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
     const dim3 slices(pmax, ls.num_rows);
     if (!have_group_max)
         hipLaunchKernelGGL(k_group_max, slices, dim3(kSliceThreads), 0, stream, scores, seq_lens,

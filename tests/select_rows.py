@@ -60,7 +60,7 @@ def crafted_rows(max_len: int, top_k: int):
     add("one past top_k", top_k + 1, rng.standard_normal(n).astype(np.float32))
     add("shorter than top_k", top_k - 3, rng.standard_normal(n).astype(np.float32))
     zeros = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0))
-    zeros[rng.choice(70000, 100, replace=False)] = rng.random(100).astype(np.float32) + 0.5
+    zeros[rng.choice(min(70000, n), 100, replace=False)] = rng.random(100).astype(np.float32) + 0.5
     add("signed zeros with a few positives", 70000, zeros)
     add("ties at the threshold (one decimal)", n,
         np.round(rng.standard_normal(n), 1).astype(np.float32))

@@ -26,6 +26,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def header_define(name):
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    m = re.search(r"#define\s+" + name + r"\s+\(?([0-9u<< ]+)\)?", text)
+    assert m, name
+    return eval(m.group(1).replace("u", ""))
+
+
+def test_binding_constants_mirror_the_header():
+    # the Python side states the header's numbers, it does not guess them
+    assert dsa.SELECT_DIRECT_MAX == header_define("DSA_SELECT_DIRECT_MAX")
+    assert dsa.NOALLOC_SCRATCH_BYTES == header_define("DSA_NOALLOC_SCRATCH_BYTES")
+
+
 def good_shape(**kw):
     f = dict(num_seqs=2, rows_per_seq=4, num_heads=64, latent_dim=512, index_heads=32,
              index_dim=128, top_k=2048, page_size=64, max_len=16388, k_capacity=16388,

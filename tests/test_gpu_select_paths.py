@@ -4,8 +4,12 @@ under (score descending, index ascending) (glm5next_dsa/layer.rs source page:
 `select_row`, and the doc of the prefill row-group selector before
 `batch_select_enabled`).
 
-Three launch shapes: rows up to 131072 tokens, rows past it (more slices
-than the others), and a top_k past 2048. The rows (tests/select_rows.py)
+Three launch shapes for the threshold filter and the finish: rows up to
+131072 tokens, rows past it (more slices than the others), and a top_k past
+2048; and three for the one-kernel selection of rows of at most 8192 tokens
+(DSA_SELECT_DIRECT_MAX), where the whole row is held and cut exactly (the
+same rows clamped to that length: all-equal, few levels, ramps, signed
+zeros, ties at the cut). The rows (tests/select_rows.py)
 reach these routes, as the CPU model of the selector confirms
 (test_select_model.py::test_gpu_route_rows_cover_every_route): rows within
 top_k; the threshold from 4-token group keys held in registers or re-read
@@ -30,7 +34,15 @@ ROUTES = {
     "131072 tokens": (131072, 2048),
     "135168 tokens": (135168, 2048),
     "top_k 2304": (131072, 2304),
+    "8192 tokens, one kernel": (8192, 2048),
+    "8192 tokens, top_k 100, one kernel": (8192, 100),
+    "6000 tokens, one kernel": (6000, 2048),
 }
+
+
+def test_one_kernel_routes_are_the_short_ones():
+    assert all((max_len <= dsa.SELECT_DIRECT_MAX) == ("one kernel" in name)
+               for name, (max_len, _) in ROUTES.items())
 
 
 @pytest.mark.parametrize("route", list(ROUTES))
@@ -41,8 +53,9 @@ def test_every_selector_route_is_exact(route):
     print(f"route {route}: max_len {MAX_LEN}, top_k {TOP_K}, {R} rows", flush=True)
     shape = dsa.Shape(num_seqs=R, rows_per_seq=1, num_heads=8, latent_dim=512, index_heads=4,
                       index_dim=64, top_k=TOP_K, page_size=64, max_len=MAX_LEN,
-                      k_capacity=MAX_LEN, max_blocks_per_seq=MAX_LEN // 64, num_pages=1)
+                      k_capacity=MAX_LEN, max_blocks_per_seq=(MAX_LEN + 63) // 64, num_pages=1)
     stride = dsa.score_stride(shape)
+    assert stride >= MAX_LEN, "the launch shape is refused"
     padded = np.full((R, stride), np.nan, np.float32)  # past L: never read
     lens = np.zeros(R, np.int32)
     for r, (_, L, vals) in enumerate(rows):
