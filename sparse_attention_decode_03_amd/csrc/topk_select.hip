@@ -113,7 +113,7 @@ __device__ uint32_t find_bin(const uint32_t *h, int nbins, uint32_t need, BinSea
 // Block-wide minimum and maximum of one pair per thread (one barrier; call
 // at most once per kernel, as the exchange words are not guarded for reuse).
 template <int NT>
-__device__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
+__device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSearch *bs)
 {
     constexpr int NW = NT / kWave;
     lo = wave_min_u32(lo);
@@ -355,7 +355,7 @@ __device__ __forceinline__ uint32_t spread8(uint32_t x)
     return x;
 }
 
-__device__ __noinline__ void select_row_full(const float *__restrict__ scores, int r, int L, int32_t *out,
+__device__ __forceinline__ void select_row_full(const float *__restrict__ scores, int r, int L, int32_t *out,
                                 u32x2 *rspill, uint32_t *gbitmap_row, int stride, int top_k,
                                 uint32_t (*hsub)[kHistBins], u32x2 *cbuf, uint32_t *lbitmap,
                                 BinSearch *bs, uint32_t *ccount)
