@@ -142,7 +142,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long",
-                    choices=["tiny", "single", "batched", "kverify", "long"])
+                    choices=["tiny", "single", "batched", "kverify", "long", "rowgroup"])
     ap.add_argument("--replicas", type=int, default=4,
                     help="input copies the steps rotate through (1 = warm caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

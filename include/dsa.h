@@ -250,6 +250,14 @@ int dsa_decode_k_noalloc(const dsa_shape *shape, const void *q_idx, const float 
  *                  [0, L_r / kp) read. How the pages form pool scores (their
  *                  gate and positional terms) is not on the pages: the
  *                  caller supplies them.
+ *   pool_valid     [S, dsa_pool_score_stride(shape, kp)] uint8, or NULL (every
+ *                  visible pool complete): the second term of the pages'
+ *                  candidacy test (pool_valid[p] && end_c <= q_pos[r]); a
+ *                  pool of sequence s marked 0 is no candidate of its rows.
+ *                  A row then takes its top min(row_select_k, candidates)
+ *                  pools; their tokens come first, the places of the pools
+ *                  it could not fill are -1, and the tail still starts at
+ *                  slot row_select_k * kp.
  *   seq_lens       [R] int32
  *   sel            [R, top_k * kp + kp - 1] int32 (output): the selected
  *                  pools' tokens in ascending pool order, then the tail, then
@@ -261,8 +269,8 @@ int dsa_decode_k_noalloc(const dsa_shape *shape, const void *q_idx, const float 
 size_t dsa_pooled_workspace_bytes(const dsa_shape *shape, int32_t kp);
 size_t dsa_pool_score_stride(const dsa_shape *shape, int32_t kp);
 int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool_scores,
-                           const int32_t *seq_lens, int32_t *sel, void *ws, size_t ws_bytes,
-                           void *stream);
+                           const uint8_t *pool_valid, const int32_t *seq_lens, int32_t *sel,
+                           void *ws, size_t ws_bytes, void *stream);
 
 /*
  * The cache-write side that feeds the path (the step before it): row r
@@ -278,6 +286,10 @@ int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool
  *     k_b of k_proj[r] (module header, second trap), var the population
  *     variance, stored as bf16 (nearest-even) at k_normed[s][pos]
  *     (`indexer_forward`).
+ *   validity mark: valid[s][pos] = 1, written with the key row (the same
+ *     condition), when valid is not NULL (`indexer_forward`: placement and
+ *     the mark both from the device position, so a captured graph does not
+ *     freeze the address).
  * Norm sums run in fp32. Rows with seq_lens[r] outside [1, max_len] write
  * nothing; two rows of one sequence must not name the same position.
  *   kv_a     [R, latent_dim] bf16     latent_w [latent_dim] bf16
@@ -285,12 +297,14 @@ int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool
  *   seq_lens [R] int32                block_tables [S, max_blocks_per_seq] int32
  *   kv_cache [num_pages, page_size, latent_dim] E4M3 bytes (updated in place)
  *   k_normed [S, k_capacity, index_dim] bf16 (updated in place)
+ *   valid    [S, k_capacity] uint8 (updated in place) or NULL
  * eps >= 0 and finite; kv_scale > 0 and finite.
  */
 int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent_w,
                     const void *k_proj, const void *k_w, const void *k_b,
                     const int32_t *seq_lens, const int32_t *block_tables, float eps,
-                    float kv_scale, uint8_t *kv_cache, void *k_normed, void *stream);
+                    float kv_scale, uint8_t *kv_cache, void *k_normed, uint8_t *valid,
+                    void *stream);
 
 /*
  * Row stride, in floats, of every scores buffer for `shape`: max_len rounded

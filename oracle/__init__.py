@@ -71,7 +71,7 @@ def _load() -> ctypes.CDLL:
     lib.oracle_layernorm_row.argtypes = [i32, P, P, P, ctypes.c_double, P, P]
     lib.oracle_layernorm_row.restype = i32
     lib.oracle_cache_write.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, i64, i64, i64,
-                                       i64, ctypes.c_double, ctypes.c_double, P, P]
+                                       i64, ctypes.c_double, ctypes.c_double, P, P, P]
     lib.oracle_cache_write.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
@@ -146,21 +146,28 @@ def topk(scores, seq_lens, top_k: int) -> np.ndarray:
     return sel
 
 
-def pooled_select(pool_scores, seq_lens, kp: int, select_k: int) -> np.ndarray:
+def pooled_select(pool_scores, seq_lens, kp: int, select_k: int, pool_valid=None,
+                  rows_per_seq: int = 1) -> np.ndarray:
     """Pooled selection and its expansion to tokens: sel [R, select_k*kp + kp - 1]
     int32, -1 padded.
 
     Follows the doc of the prefill row-group selector on the glm5next_dsa
     layer.rs source page: pool p (tokens p*kp .. p*kp + kp - 1) is a candidate
-    of a row only when it is complete and its last token is visible to the
-    row's query, i.e. p < (q_pos + 1) / kp = L // kp; the row takes
-    row_select_k = min(select_k, L // kp) pools under the total order (score
-    descending, pool index ascending); the selected pools expand to their kp
-    tokens each, and the row's visible tail (tokens L // kp * kp .. L - 1, the
-    incomplete pool) is written from slot row_select_k * kp on.
+    of a row only when it is complete (pool_valid[p]) and its last token is
+    visible to the row's query, i.e. p < (q_pos + 1) / kp = L // kp; the row
+    expands row_select_k = min(select_k, L // kp) pool places (the per-row
+    correction of the expansion), filled by its top candidates under the
+    total order (score descending, pool index ascending); the selected pools
+    expand to their kp tokens each, and the row's visible tail (tokens
+    L // kp * kp .. L - 1, the incomplete pool) is written from slot
+    row_select_k * kp on.
     Readings: pools expand in ascending pool order (as the per-token ids are
     ascending); the pool scores are an input (how the pages form them from
-    the gate and the positional term is not on the pages)."""
+    the gate and the positional term is not on the pages); pool_valid
+    [S, >= max pools] (None: every visible pool complete) belongs to the
+    sequence, row r to sequence r // rows_per_seq; a non-candidate is never
+    taken, so a row with fewer candidates than row_select_k leaves the rest
+    of its pool places -1 and its tail where its position puts it."""
     seq_lens = _c(seq_lens, np.int32)
     R = seq_lens.shape[0]
     width = select_k * kp + kp - 1
@@ -169,12 +176,17 @@ def pooled_select(pool_scores, seq_lens, kp: int, select_k: int) -> np.ndarray:
         L = int(seq_lens[r])
         pvis = L // kp
         rsk = min(select_k, pvis)
+        cand = [p for p in range(pvis)
+                if pool_valid is None or pool_valid[r // rows_per_seq][p]]
         tokens = []
-        if pvis > 0:
-            pools = topk_row(np.asarray(pool_scores[r], dtype=np.float64)[:pvis], pvis, select_k)[:rsk]
+        if cand:
+            sc = np.asarray(pool_scores[r], dtype=np.float64)[cand]
+            order = topk_row(sc, len(cand), select_k)[:min(rsk, len(cand))]
+            pools = sorted(cand[int(i)] for i in order)
             tokens = [int(p) * kp + i for p in pools for i in range(kp)]
-        tokens += list(range(pvis * kp, L))
         out[r, :len(tokens)] = tokens
+        tail = list(range(pvis * kp, L))
+        out[r, rsk * kp:rsk * kp + len(tail)] = tail
     return out
 
 
@@ -278,10 +290,11 @@ def layernorm_row(x, w, b, eps: float):
 
 
 def cache_write(kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables, rows_per_seq: int,
-                page_size: int, eps: float, kv_scale: float, kv_cache, k_normed):
+                page_size: int, eps: float, kv_scale: float, kv_cache, k_normed, valid=None):
     """The cache-write step on copies of the caches. kv_a [R,Dl], latent_w [Dl],
     k_proj [R,D], k_w [D], k_b [D] are bf16 codes; kv_cache [pages,ps,Dl] uint8;
-    k_normed [S,cap,D] bf16 codes. Returns (kv_cache', k_normed')."""
+    k_normed [S,cap,D] bf16 codes; valid [S,cap] uint8 marks or None. Returns
+    (kv_cache', k_normed'), and valid' third when valid is given."""
     kv = _c(_bf16_values(kv_a), np.float64)
     lw = _c(_bf16_values(latent_w), np.float64)
     kp = _c(_bf16_values(k_proj), np.float64)
@@ -291,14 +304,17 @@ def cache_write(kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables, rows_p
     bt = _c(block_tables, np.int32)
     cache = np.array(kv_cache, dtype=np.uint8, copy=True, order="C")
     keys = np.array(k_normed, dtype=np.uint16, copy=True, order="C")
+    marks = None if valid is None else np.array(valid, dtype=np.uint8, copy=True, order="C")
+    if marks is not None and marks.shape != keys.shape[:2]:
+        raise ValueError("valid must be [S, k_capacity]")
     R, Dl = kv.shape
     D = kp.shape[1]
     rc = _load().oracle_cache_write(R, rows_per_seq, Dl, D, _p(kv), _p(lw), _p(kp), _p(kw),
                                     _p(kb), _p(seq_lens), _p(bt), bt.shape[1], page_size,
                                     cache.shape[0], keys.shape[1], eps, kv_scale, _p(cache),
-                                    _p(keys))
+                                    _p(keys), None if marks is None else _p(marks))
     _check(rc, "oracle_cache_write")
-    return cache, keys
+    return (cache, keys) if marks is None else (cache, keys, marks)
 
 
 def decode(inputs: dict, rows=None):

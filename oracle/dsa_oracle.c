@@ -562,7 +562,10 @@ int oracle_layernorm_row(int n, const double *x, const double *w, const double *
  *   kv_cache[page * page_size + pos % page_size] = latent row of kv_a[r]
  *     with page = block_tables[s][pos / page_size]  ([P1] `decode_k` slot
  *     computation), skipped when page is outside [0, num_pages);
- *   k_normed[s][pos] = key row of k_proj[r]  ([P1] `indexer_forward`).
+ *   k_normed[s][pos] = key row of k_proj[r]  ([P1] `indexer_forward`);
+ *   valid[s][pos] = 1 with that key row, if valid is not NULL ([P1]
+ *     `indexer_forward`: the store places the key and its validity mark
+ *     from the same device position).
  * Rows with seq_lens[r] < 1 or pos >= k_capacity write nothing. The caches
  * are updated in place (the caller passes copies). Inputs are the decoded
  * values of the bf16 operands. */
@@ -570,7 +573,7 @@ int oracle_cache_write(int R, int K, int Dl, int D, const double *kv_a, const do
                        const double *k_proj, const double *k_w, const double *k_b,
                        const int32_t *seq_lens, const int32_t *block_tables, int64_t max_blocks,
                        int64_t page_size, int64_t num_pages, int64_t k_capacity, double eps,
-                       double kv_scale, uint8_t *kv_cache, uint16_t *k_normed)
+                       double kv_scale, uint8_t *kv_cache, uint16_t *k_normed, uint8_t *valid)
 {
     if (R < 1 || K < 1 || Dl < 1 || D < 1 || page_size < 1 || !(kv_scale > 0.0))
         return ORACLE_EINVAL;
@@ -587,6 +590,8 @@ int oracle_cache_write(int R, int K, int Dl, int D, const double *kv_a, const do
         if (rc != ORACLE_OK)
             break;
         memcpy(k_normed + ((int64_t)s * k_capacity + pos) * D, c16, sizeof(uint16_t) * (size_t)D);
+        if (valid != NULL)
+            valid[(int64_t)s * k_capacity + pos] = 1; /* the mark goes with the key row */
         if (pos / page_size >= max_blocks)
             continue;
         const int32_t page = block_tables[(int64_t)s * max_blocks + pos / page_size];

@@ -11,7 +11,10 @@
 //  - indexer key row: LayerNorm with a bias (module header, second trap),
 //    (x - mean) / sqrt(var + eps) * w + b, stored as bf16 at
 //    k_normed[s][pos] (`indexer_forward`: the key row lands at the
-//    position the indexer cache advances to).
+//    position the indexer cache advances to), and, when the caller keeps
+//    them, the position's validity mark valid[s][pos] = 1 with it
+//    (`indexer_forward`: placement and the mark both from the device
+//    position, never a host-baked address).
 //
 // One workgroup per row: 256 threads normalise the 512-wide latent (two
 // values each), wave 0 also normalises the key row. Sums run in fp32 in a
@@ -48,8 +51,8 @@ __global__ __launch_bounds__(kCwThreads) void k_cache_write(
     const uint16_t *__restrict__ k_proj, const uint16_t *__restrict__ k_w,
     const uint16_t *__restrict__ k_b, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ bt, uint8_t *__restrict__ kv_cache, uint16_t *__restrict__ k_normed,
-    int K, int ps, int max_blocks, int num_pages, int64_t cap, int max_len, float eps,
-    float inv_kv_scale)
+    uint8_t *__restrict__ valid, int K, int ps, int max_blocks, int num_pages, int64_t cap,
+    int max_len, float eps, float inv_kv_scale)
 {
     __shared__ float part[kCwThreads / kWave];
     const int r = blockIdx.x;
@@ -110,24 +113,29 @@ __global__ __launch_bounds__(kCwThreads) void k_cache_write(
                             bf16_bits_to_f32(k_b[V * lane + i]);
             dst[i] = f32_to_bf16_rne(y);
         }
+        if (valid != nullptr && lane == 0)
+            valid[(int64_t)s * cap + pos] = 1;
     }
 }
 
 int launch_cache_write(const LaunchShape &ls, const uint16_t *kv_a, const uint16_t *latent_w,
                        const uint16_t *k_proj, const uint16_t *k_w, const uint16_t *k_b,
                        const int32_t *seq_lens, const int32_t *block_tables, float eps,
-                       float kv_scale, uint8_t *kv_cache, uint16_t *k_normed, hipStream_t stream)
+                       float kv_scale, uint8_t *kv_cache, uint16_t *k_normed, uint8_t *valid,
+                       hipStream_t stream)
 {
     const float inv = (float)(1.0 / (double)kv_scale);
     if (ls.index_dim == 128)
         hipLaunchKernelGGL(k_cache_write<128>, dim3(ls.num_rows), dim3(kCwThreads), 0, stream,
                            kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables, kv_cache,
-                           k_normed, ls.rows_per_seq, ls.page_size, ls.max_blocks, ls.num_pages,
+                           k_normed, valid, ls.rows_per_seq, ls.page_size, ls.max_blocks,
+                           ls.num_pages,
                            (int64_t)ls.k_capacity, ls.max_len, eps, inv);
     else if (ls.index_dim == 64)
         hipLaunchKernelGGL(k_cache_write<64>, dim3(ls.num_rows), dim3(kCwThreads), 0, stream,
                            kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables, kv_cache,
-                           k_normed, ls.rows_per_seq, ls.page_size, ls.max_blocks, ls.num_pages,
+                           k_normed, valid, ls.rows_per_seq, ls.page_size, ls.max_blocks,
+                           ls.num_pages,
                            (int64_t)ls.k_capacity, ls.max_len, eps, inv);
     else
         return -1;

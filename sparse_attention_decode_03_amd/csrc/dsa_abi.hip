@@ -116,7 +116,7 @@ constexpr int kMaxPoolTokens = 1024; // kp above this is refused
 struct PooledLayout {
     dsa::LaunchShape ls_pool;
     dsa::Workspace wl;
-    size_t pool_lens, sel_pools, total;
+    size_t pool_lens, sel_pools, masked, total;
     int max_len; // the token ceiling
     bool any_pool;
 };
@@ -139,6 +139,8 @@ int pooled_layout(const dsa_shape *shape, int32_t kp, PooledLayout *pl)
     off = align256(off + (size_t)ls.num_rows * sizeof(int32_t));
     pl->sel_pools = off;
     off = align256(off + (size_t)ls.num_rows * ls.top_k * sizeof(int32_t));
+    pl->masked = off; // pool scores with the incomplete pools at -inf (pool_valid given)
+    off = align256(off + (size_t)ls.num_rows * (size_t)dsa::score_stride(pl->ls_pool) * sizeof(float));
     pl->total = off;
     return DSA_OK;
 }
@@ -251,8 +253,8 @@ size_t dsa_pool_score_stride(const dsa_shape *shape, int32_t kp)
 }
 
 int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool_scores,
-                           const int32_t *seq_lens, int32_t *sel, void *ws, size_t ws_bytes,
-                           void *stream)
+                           const uint8_t *pool_valid, const int32_t *seq_lens, int32_t *sel,
+                           void *ws, size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     PooledLayout pl;
@@ -262,14 +264,17 @@ int dsa_topk_select_pooled(const dsa_shape *shape, int32_t kp, const float *pool
     if ((rc = check_ptr(pool_scores, "pool_scores")) || (rc = check_ptr(seq_lens, "seq_lens")) ||
         (rc = check_ptr(sel, "sel")))
         return rc;
+    if (pool_valid != nullptr && ((uintptr_t)pool_valid % 16) != 0)
+        return fail(DSA_EINVAL, "pool_valid is not 16-byte aligned");
     if (check_ptr(ws, "ws") != DSA_OK)
         return fail(DSA_EWORKSPACE, "workspace is NULL or not 16-byte aligned");
     if (ws_bytes < pl.total)
         return fail(DSA_EWORKSPACE, "workspace of %zu bytes is below the %zu this shape needs",
                     ws_bytes, pl.total);
-    return launched(dsa::launch_select_pooled(pl.ls_pool, pl.max_len, kp, pool_scores, seq_lens,
-                                              sel, (char *)ws, pl.wl, pl.pool_lens, pl.sel_pools,
-                                              pl.any_pool, (hipStream_t)stream),
+    return launched(dsa::launch_select_pooled(pl.ls_pool, pl.max_len, kp, pool_scores, pool_valid,
+                                              seq_lens, sel, (char *)ws, pl.wl, pl.pool_lens,
+                                              pl.sel_pools, pl.masked, pl.any_pool,
+                                              (hipStream_t)stream),
                     "select_pooled");
 }
 
@@ -457,7 +462,8 @@ int dsa_decode_k_noalloc(const dsa_shape *shape, const void *q_idx, const float 
 int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent_w,
                     const void *k_proj, const void *k_w, const void *k_b,
                     const int32_t *seq_lens, const int32_t *block_tables, float eps,
-                    float kv_scale, uint8_t *kv_cache, void *k_normed, void *stream)
+                    float kv_scale, uint8_t *kv_cache, void *k_normed, uint8_t *valid,
+                    void *stream)
 {
     g_err[0] = 0;
     dsa::LaunchShape ls;
@@ -477,7 +483,7 @@ int dsa_cache_write(const dsa_shape *shape, const void *kv_a, const void *latent
     return launched(dsa::launch_cache_write(ls, (const uint16_t *)kv_a, (const uint16_t *)latent_w,
                                             (const uint16_t *)k_proj, (const uint16_t *)k_w,
                                             (const uint16_t *)k_b, seq_lens, block_tables, eps,
-                                            kv_scale, kv_cache, (uint16_t *)k_normed,
+                                            kv_scale, kv_cache, (uint16_t *)k_normed, valid,
                                             (hipStream_t)stream),
                     "cache_write");
 }

@@ -98,14 +98,18 @@ int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq
 // ls_pool is the token shape with max_len = max(1, max_len / kp); pool counts
 // and selected pools live in the workspace at the given offsets; any_pool
 // false (max_len < kp) skips the selection (every row keeps its tail only).
+// pool_valid [S][score_stride(ls_pool)] (may be null): a pool marked 0 is no
+// candidate (its score goes to -inf in the `masked` region before the
+// selection, and the expansion drops it if it was still taken).
 int launch_select_pooled(const LaunchShape &ls_pool, int max_len, int kp, const float *pool_scores,
-                         const int32_t *seq_lens, int32_t *sel, char *ws, const Workspace &wl,
-                         size_t pool_lens_off, size_t sel_pools_off, bool any_pool,
-                         hipStream_t stream);
+                         const uint8_t *pool_valid, const int32_t *seq_lens, int32_t *sel, char *ws,
+                         const Workspace &wl, size_t pool_lens_off, size_t sel_pools_off,
+                         size_t masked_off, bool any_pool, hipStream_t stream);
 int launch_cache_write(const LaunchShape &ls, const uint16_t *kv_a, const uint16_t *latent_w,
                        const uint16_t *k_proj, const uint16_t *k_w, const uint16_t *k_b,
                        const int32_t *seq_lens, const int32_t *block_tables, float eps,
-                       float kv_scale, uint8_t *kv_cache, uint16_t *k_normed, hipStream_t stream);
+                       float kv_scale, uint8_t *kv_cache, uint16_t *k_normed, uint8_t *valid,
+                       hipStream_t stream);
 // t_att / t_merge time the attention and the merge kernels; with a single
 // chunk there is no merge and t_merge's events, if any, are recorded right
 // after the attention (a span of about zero).

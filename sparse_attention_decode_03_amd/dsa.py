@@ -121,7 +121,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_decode_k_timed.restype = i32
     lib.dsa_decode_k_noalloc.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P]
     lib.dsa_decode_k_noalloc.restype = i32
-    lib.dsa_cache_write.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P]
+    lib.dsa_cache_write.argtypes = [S, P, P, P, P, P, P, P, f32, f32, P, P, P, P]
     lib.dsa_cache_write.restype = i32
     lib.dsa_score_stride.argtypes = [S]
     lib.dsa_score_stride.restype = sz
@@ -129,7 +129,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_pooled_workspace_bytes.restype = sz
     lib.dsa_pool_score_stride.argtypes = [S, i32]
     lib.dsa_pool_score_stride.restype = sz
-    lib.dsa_topk_select_pooled.argtypes = [S, i32, P, P, P, P, sz, P]
+    lib.dsa_topk_select_pooled.argtypes = [S, i32, P, P, P, P, P, sz, P]
     lib.dsa_topk_select_pooled.restype = i32
     lib.dsa_bt_entries_needed.argtypes = [sz, sz, sz]
     lib.dsa_bt_entries_needed.restype = sz
@@ -203,11 +203,13 @@ def pool_score_stride(shape: Shape, kp: int) -> int:
 
 
 def topk_select_pooled(shape: Shape, kp: int, pool_scores, seq_lens, sel, ws,
-                       ws_bytes: Optional[int] = None, stream=None) -> None:
+                       ws_bytes: Optional[int] = None, stream=None, pool_valid=None) -> None:
+    """dsa_topk_select_pooled; pool_valid ([S, pool stride] uint8, or None)
+    gates candidacy."""
     nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(load().dsa_topk_select_pooled(ctypes.byref(shape), kp, _ptr(pool_scores),
-                                         _ptr(seq_lens), _ptr(sel), _ptr(ws), nb,
-                                         _stream(stream)))
+                                         _ptr(pool_valid), _ptr(seq_lens), _ptr(sel), _ptr(ws),
+                                         nb, _stream(stream)))
 
 
 def mla_decode(shape: Shape, q, kv_cache, block_tables, seq_lens, sel, kv_scale: float,
@@ -270,10 +272,13 @@ def decode_k_noalloc(shape: Shape, q_idx, w, k_normed, q, kv_cache, block_tables
 
 
 def cache_write(shape: Shape, kv_a, latent_w, k_proj, k_w, k_b, seq_lens, block_tables,
-                eps: float, kv_scale: float, kv_cache, k_normed, stream=None) -> None:
+                eps: float, kv_scale: float, kv_cache, k_normed, valid=None, stream=None) -> None:
+    """dsa_cache_write; valid ([S, k_capacity] uint8, or None) receives the
+    validity marks."""
     _check(load().dsa_cache_write(ctypes.byref(shape), _ptr(kv_a), _ptr(latent_w), _ptr(k_proj),
                                   _ptr(k_w), _ptr(k_b), _ptr(seq_lens), _ptr(block_tables), eps,
-                                  kv_scale, _ptr(kv_cache), _ptr(k_normed), _stream(stream)))
+                                  kv_scale, _ptr(kv_cache), _ptr(k_normed),
+                                  None if valid is None else _ptr(valid), _stream(stream)))
 
 
 class DeviceStep:

@@ -66,7 +66,10 @@ class Workload:
         return self.num_seqs * self.rows_per_seq
 
 
-# The five workloads of the benchmark, in order (seeds 0..4).
+# The five workloads of the benchmark, in order (seeds 0..4), and the
+# row-group shape: 16 consecutive query rows of a sequence selected in one
+# pass, as the pages' prefill does it (layer.rs, the prefill row-group
+# selector, 16 rows of a 9,000-token prefill), here for 8 sequences.
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", 1, 1, 8, 4, 64, 64, 16, seed=0, context=256),
     "single": Workload("single", 1, 1, 64, 32, 128, 2048, 64, seed=1, context=8192),
@@ -76,6 +79,8 @@ WORKLOADS: Dict[str, Workload] = {
                         lengths="verify", base=16384),
     "long": Workload("long", 8, 1, 64, 32, 128, 2048, 64, seed=4, context=131072,
                      key_dist="student_t3"),
+    "rowgroup": Workload("rowgroup", 8, 16, 64, 32, 128, 2048, 64, seed=5,
+                         lengths="verify", base=9000),
 }
 
 

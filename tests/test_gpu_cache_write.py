@@ -74,14 +74,19 @@ def run_case(kv_scale, seed):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     d_cache = dev(cache0)
     d_keys = dev(keys0.view(np.int16))
+    valid0 = (rng.random((S, max_len)) < 0.3).astype(np.uint8)  # earlier marks stay
+    d_valid = dev(valid0)
     dsa.cache_write(shape, dev(kv_a.view(np.int16)), dev(latent_w.view(np.int16)),
                     dev(k_proj.view(np.int16)), dev(k_w.view(np.int16)), dev(k_b.view(np.int16)),
-                    dev(seq_lens), dev(bt), eps, kv_scale, d_cache, d_keys)
+                    dev(seq_lens), dev(bt), eps, kv_scale, d_cache, d_keys, valid=d_valid)
     torch.cuda.synchronize()
     got_cache = d_cache.cpu().numpy()
     got_keys = d_keys.cpu().numpy().view(np.uint16)
-    ref_cache, ref_keys = oracle.cache_write(kv_a, latent_w, k_proj, k_w, k_b, seq_lens, bt, K,
-                                             ps, eps, kv_scale, cache0, keys0)
+    ref_cache, ref_keys, ref_valid = oracle.cache_write(kv_a, latent_w, k_proj, k_w, k_b, seq_lens,
+                                                        bt, K, ps, eps, kv_scale, cache0, keys0,
+                                                        valid=valid0)
+    # validity marks: byte for byte (set with each written key row, nothing else)
+    np.testing.assert_array_equal(d_valid.cpu().numpy(), ref_valid)
 
     # untouched everywhere the oracle did not write
     written_slots = set()

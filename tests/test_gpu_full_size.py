@@ -1,10 +1,11 @@
-"""The five workloads at their full sizes, through dsa_decode_k in the launch
+"""The benchmark's workloads at their full sizes, through dsa_decode_k in the launch
 configuration the benchmark times, checked row by row against the CPU
 oracle: scores within tolerance; selection exact on the GPU's own scores and,
 end to end, equal to the oracle's own selection on its fp64 scores except for
 tokens within 1e-6 relative of a row's cut; attention within the 2e-2
 contract and the bound derived from the kernel's roundings, over the GPU's
-own selection. Each case prints its largest errors."""
+own selection. The row-group workload (8 sequences x 16 rows) checks the rows
+of its first and last sequence. Each case prints its largest errors."""
 import pytest
 
 from sparse_attention_decode_03_amd import workloads as wl
@@ -15,13 +16,16 @@ from gpu_common import (check_attention, check_scores, check_selection,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["tiny", "single", "batched", "kverify", "long"])
+@pytest.mark.parametrize("name", ["tiny", "single", "batched", "kverify", "long", "rowgroup"])
 def test_full_size_workload(name):
     inputs = wl.make_inputs(wl.WORKLOADS[name])
     print(f"workload {name}: {len(inputs['seq_lens'])} rows", flush=True)
     step = run_step(inputs)
     scores, sel, out = host(step)
     rows = range(inputs["seq_lens"].shape[0])
+    if name == "rowgroup":
+        K, S = inputs["rows_per_seq"], inputs["num_seqs"]
+        rows = list(range(K)) + list(range((S - 1) * K, S * K))
     refs, score_worst = check_scores(inputs, scores, rows)
     check_selection(inputs, scores, sel, rows)
     differ = check_selection_end_to_end(inputs, refs, sel, rows)

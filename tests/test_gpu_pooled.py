@@ -14,7 +14,8 @@ from gpu_common import assert_attention_row, bf16_codes_to_f64, small
 pytestmark = pytest.mark.gpu
 
 
-def run_pooled(lens, kp, select_k, scores_fn, max_len=None, seed=0):
+def run_pooled(lens, kp, select_k, scores_fn, max_len=None, seed=0, valid_frac=None,
+               past_fill=np.nan):
     lens = np.asarray(lens, np.int32)
     R = lens.shape[0]
     max_len = int(lens.max()) if max_len is None else max_len
@@ -24,21 +25,25 @@ def run_pooled(lens, kp, select_k, scores_fn, max_len=None, seed=0):
                    num_pages=R * ((max_len + 63) // 64 + 1))
     stride = dsa.pool_score_stride(sh, kp)
     rng = np.random.default_rng(seed)
-    scores = np.full((R, stride), np.nan, np.float32)   # entries past a row's pools are never read
+    scores = np.full((R, stride), past_fill, np.float32)  # entries past a row's pools are never read
     for r in range(R):
         npool = int(lens[r]) // kp
         scores[r, :npool] = scores_fn(rng, npool)
+    pool_valid = None
+    if valid_frac is not None:
+        pool_valid = (rng.random((R, stride)) < valid_frac).astype(np.uint8)
     width = select_k * kp + kp - 1
     print(f"pooled: R={R} kp={kp} select_k={select_k} max_len={max_len}", flush=True)
     d_scores = torch.from_numpy(scores).cuda()
     d_lens = torch.from_numpy(lens).cuda()
     d_sel = torch.full((R, width), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(dsa.pooled_workspace_bytes(sh, kp), dtype=torch.uint8, device="cuda")
-    dsa.topk_select_pooled(sh, kp, d_scores, d_lens, d_sel, ws)
+    d_valid = None if pool_valid is None else torch.from_numpy(pool_valid).cuda()
+    dsa.topk_select_pooled(sh, kp, d_scores, d_lens, d_sel, ws, pool_valid=d_valid)
     torch.cuda.synchronize()
     got = d_sel.cpu().numpy()
-    want = oracle.pooled_select(np.nan_to_num(scores, nan=0.0).astype(np.float64), lens, kp,
-                                select_k)
+    want = oracle.pooled_select(np.nan_to_num(scores, nan=0.0, posinf=0.0).astype(np.float64),
+                                lens, kp, select_k, pool_valid=pool_valid)
     np.testing.assert_array_equal(got, want)
     return sh, scores, lens, got
 
@@ -56,6 +61,27 @@ ties = lambda rng, n: rng.integers(-2, 3, size=n).astype(np.float32)
 ])
 def test_pooled_selection_matches_the_oracle(kp, select_k, lens, fn):
     run_pooled(lens, kp, select_k, fn, seed=kp * 7 + select_k)
+
+
+@pytest.mark.parametrize("kp,select_k,lens,frac", [
+    (4, 64, [1000, 3, 4, 257, 640], 0.8),      # some rows with fewer candidates than places
+    (16, 32, [5000, 700, 4096], 0.97),
+    (4, 2048, [131072, 9000, 8191], 0.9),
+    (8, 16, [400, 64, 200], 0.0),              # no pool complete: pool places -1, tails kept
+])
+def test_incomplete_pools_are_no_candidates(kp, select_k, lens, frac):
+    # layer.rs, the prefill row-group selector: pool_valid[p] is the second
+    # term of the candidacy test
+    run_pooled(lens, kp, select_k, normal, seed=kp * 11 + select_k, valid_frac=frac)
+
+
+def test_a_longer_pool_walk_changes_neither_set_nor_order():
+    # layer.rs, same doc: walking more pools than a row sees (the group's
+    # count) reaches the same top-select_k set and order. Here every entry
+    # past a row's pools holds +inf: a walk that read one would take it.
+    got_wide = run_pooled([3000, 517, 4096], 4, 128, normal, seed=3, past_fill=np.inf)[3]
+    got = run_pooled([3000, 517, 4096], 4, 128, normal, seed=3)[3]
+    np.testing.assert_array_equal(got_wide, got)
 
 
 def test_one_token_pools_equal_the_token_selector():

@@ -420,6 +420,34 @@ def test_cache_write_slot_arithmetic_and_untouched_elsewhere():
     assert np.argwhere((k3 != keys).any(axis=2)).tolist() == [[0, 5], [1, 1]]
 
 
+
+def test_validity_marks_follow_the_key_rows_and_form_a_prefix():
+    """The mark goes with the key row (layer.rs `indexer_forward`: the key
+    and its validity mark are placed from the same device position). Writing
+    a sequence's tokens one step at a time (positions 0, 1, 2, ...) leaves
+    exactly the written prefix marked; an out-of-range row marks nothing, and
+    a row whose latent page is unmapped still marks its position."""
+    Dl, D, ps, cap = 8, 4, 4, 12
+    rng = np.random.default_rng(13)
+    lw, kw, kb = bf16(np.ones(Dl)), bf16(np.ones(D)), bf16(np.zeros(D))
+    bt = np.array([[3, 0, 2], [-1, -1, -1]], np.int32)  # sequence 1: no latent page at all
+    cache = np.zeros((4, ps, Dl), np.uint8)
+    keys = np.zeros((2, cap, D), np.uint16)
+    valid = np.zeros((2, cap), np.uint8)
+    for step in range(1, 8):
+        kv_a = bf16(rng.standard_normal((2, Dl)))
+        k_proj = bf16(rng.standard_normal((2, D)))
+        lens = np.array([step, step if step <= 5 else 0], np.int32)  # row 1 stops after 5
+        cache, keys, valid = oracle.cache_write(kv_a, lw, k_proj, kw, kb, lens, bt, 1, ps, 1e-6,
+                                                1.0, cache, keys, valid=valid)
+        assert valid[0].tolist() == [1] * step + [0] * (cap - step)
+        assert valid[1].tolist() == [1] * min(step, 5) + [0] * (cap - min(step, 5))
+    # a row past the capacity writes no key and no mark
+    _, _, v2 = oracle.cache_write(bf16(np.ones((1, Dl))), lw, bf16(np.ones((1, D))), kw, kb,
+                                  np.array([cap + 1], np.int32), bt[:1], 1, ps, 1e-6, 1.0, cache,
+                                  keys[:1], valid=valid[:1])
+    np.testing.assert_array_equal(v2, valid[:1])
+
 # ---------------------------------------------------------------------------
 # Softmax weights, the attention error scale and the end-to-end pipeline at
 # K > 1, each against torch's casts and softmax on the definitions.

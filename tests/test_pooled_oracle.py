@@ -85,3 +85,79 @@ def test_the_tail_base_is_the_row_own_selection_size():
     out = oracle.pooled_select(np.arange(8.0)[None, :], [11], 4, 6)
     np.testing.assert_array_equal(out[0, :11], np.arange(11))
     assert (out[0, 11:] == -1).all()
+
+
+# ---------------------------------------------------------------------------
+# pool_valid, the second term of the candidacy test (same doc: "a pool is a
+# candidate only when it is complete AND its last token is visible").
+
+def test_all_pools_complete_is_the_ungated_selection():
+    rng = np.random.default_rng(21)
+    scores = rng.standard_normal((5, 120))
+    lens = np.array([120, 7, 64, 33, 119], np.int32)
+    ones = np.ones((5, 120), np.uint8)
+    for kp, select_k in ((4, 6), (1, 40), (8, 2)):
+        np.testing.assert_array_equal(
+            oracle.pooled_select(scores, lens, kp, select_k, pool_valid=ones),
+            oracle.pooled_select(scores, lens, kp, select_k))
+
+
+@pytest.mark.parametrize("kp", [2, 4, 8])
+def test_an_incomplete_pool_is_the_pool_scored_minus_infinity(kp):
+    # While a row has at least row_select_k candidates, marking a pool
+    # incomplete selects exactly what scoring it -inf (the pages' -FLT_MAX,
+    # below every candidate) selects in the ungated walk, and changes
+    # nothing if the pool was not selected.
+    rng = np.random.default_rng(kp + 30)
+    for trial in range(40):
+        npool = int(rng.integers(3, 12))
+        L = npool * kp + int(rng.integers(0, kp))
+        scores = rng.integers(-3, 4, size=(1, npool)).astype(np.float64)
+        select_k = int(rng.integers(1, npool))
+        valid = np.ones((1, npool), np.uint8)
+        off = rng.choice(npool, size=int(rng.integers(1, npool - select_k + 1)), replace=False)
+        valid[0, off] = 0
+        masked = scores.copy()
+        masked[0, off] = -np.inf
+        np.testing.assert_array_equal(
+            oracle.pooled_select(scores, [L], kp, select_k, pool_valid=valid),
+            oracle.pooled_select(masked, [L], kp, select_k))
+        # a pool that is not selected anyway may be marked incomplete freely
+        base = oracle.pooled_select(scores, [L], kp, select_k)
+        chosen = set(int(t) // kp for t in base[0, :select_k * kp])
+        free = [p for p in range(npool) if p not in chosen]
+        if free:
+            v2 = np.ones((1, npool), np.uint8)
+            v2[0, free[0]] = 0
+            np.testing.assert_array_equal(
+                oracle.pooled_select(scores, [L], kp, select_k, pool_valid=v2), base)
+
+
+def test_too_few_candidates_leave_pool_places_empty_and_the_tail_in_place():
+    # 5 pools visible, select_k 4, only pools 1 and 3 complete: their tokens,
+    # then -1 for the two places that no candidate fills, then the tail at
+    # slot 4 * kp (the row's position alone sets it)
+    kp = 4
+    scores = np.array([[5.0, 1.0, 9.0, 2.0, 7.0]])
+    valid = np.array([[0, 1, 0, 1, 0]], np.uint8)
+    out = oracle.pooled_select(scores, [22], kp, 4, pool_valid=valid)
+    np.testing.assert_array_equal(out[0, :8], [4, 5, 6, 7, 12, 13, 14, 15])
+    assert (out[0, 8:16] == -1).all()
+    np.testing.assert_array_equal(out[0, 16:18], [20, 21])
+    assert (out[0, 18:] == -1).all()
+    # no complete pool at all: only the tail
+    out = oracle.pooled_select(scores, [22], kp, 4, pool_valid=np.zeros((1, 5), np.uint8))
+    assert (out[0, :16] == -1).all()
+    np.testing.assert_array_equal(out[0, 16:18], [20, 21])
+
+
+def test_rows_of_one_sequence_share_its_pool_marks():
+    rng = np.random.default_rng(40)
+    scores = rng.standard_normal((4, 12))
+    lens = np.array([40, 44, 48, 47], np.int32)   # two sequences of two rows
+    valid = (rng.random((2, 12)) < 0.6).astype(np.uint8)
+    got = oracle.pooled_select(scores, lens, 4, 5, pool_valid=valid, rows_per_seq=2)
+    for r in range(4):
+        one = oracle.pooled_select(scores[r:r + 1], lens[r:r + 1], 4, 5,
+                                   pool_valid=valid[r // 2:r // 2 + 1])
+        np.testing.assert_array_equal(got[r], one[0])
