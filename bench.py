@@ -151,8 +151,8 @@ def main() -> int:
                     help="time the pooled selection (pools of this many tokens, top_k / kp "
                          "pools per row, synthetic pool scores) instead of the decode step")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="only launch the index kernel and a plain 256 MiB device copy a few "
-                         "times each (for rocprofv3 counter passes), then exit")
+                    help="only run four decode steps and a plain 256 MiB device copy four "
+                         "times (for rocprofv3 counter passes), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -186,7 +186,8 @@ def main() -> int:
         return bench_pooled(args, wlk, inputs, sh)
 
     if args.traffic_probe:
-        # HBM counters read per dispatch: the index kernel, and a plain copy of
+        # HBM counters read per dispatch: four decode steps (their index pass
+        # is the dominant kernel the roofline times), and a plain copy of
         # known size that calibrates the counter's scale
         copy_bytes = 256 << 20
         src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
@@ -196,8 +197,7 @@ def main() -> int:
             for i in range(4):
                 dst.copy_(src)
             for i in range(4):
-                dsa.index_scores(sh, step.q_idx, step.w, keys[i % nrep], step.seq_lens,
-                                 step.scores, stream=stream)
+                run(i)
         torch.cuda.synchronize()
         print(json.dumps({"traffic_probe": True, "copy_bytes": copy_bytes,
                           "index_algorithmic_bytes": algorithmic_bytes(inputs)["index"],
