@@ -7,9 +7,9 @@
 // cache is read token-major as k[raw * D + d]).
 //
 // Design (HBM-bound: 256 B of keys per token at D = 128 against 8 kflop):
-//  - One workgroup walks every W-th 256-token tile of one sequence and scores
-//    each tile for every row of that sequence (the K rows of a verify share
-//    one key read). Keys stream HBM -> VGPR with fully coalesced 16-byte
+//  - One workgroup walks every W-th tile of one sequence (256 tokens; 128
+//    when two or four rows share the keys) and scores each tile for every
+//    row of that sequence (the K rows of a verify share one key read). Keys stream HBM -> VGPR with fully coalesced 16-byte
 //    loads (the next tile's loads are in flight while the current tile
 //    computes) and are parked in LDS with an XOR swizzle, then re-read in
 //    matrix-core operand order without bank conflicts.
@@ -35,7 +35,7 @@ namespace dsa {
 constexpr int kIdxThreads = 256; // 4 waves x 64 tokens of a tile
 constexpr int kIdxWgTarget = 512; // workgroups the tiles of a call spread over
 
-// LDS: the key tile, 256 tokens x 16 chunks of 16 bytes (64 KiB at D = 128).
+// LDS: the key tile, up to 256 tokens x 16 chunks of 16 bytes (64 KiB at D = 128).
 
 // The epilogue of one 32-token block of one row from its 32x32 MFMA result
 // (lane: token t, 16 head partials): ReLU-weighted head sum, the score store
@@ -75,7 +75,7 @@ __device__ __forceinline__ void block_epilogue(const float (&wv)[16], const floa
     }
 }
 
-template <int D, bool ONE_ROW, bool GM>
+template <int D, bool ONE_ROW, bool GM, int TILE>
 __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint16_t *__restrict__ k_normed, const int32_t *__restrict__ seq_lens,
@@ -84,8 +84,11 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 {
     constexpr int CH = D / 8;  // 16-byte chunks per key row
     constexpr int KS = D / 16; // MFMA k-steps
-    constexpr int LOADS = kIdxTile * CH / kIdxThreads;
-    __shared__ u32x4 lds[kIdxTile * CH];
+    // TILE tokens per tile: 256 with one row, 128 or 256 with K rows (see
+    // rows_tile); the single-row walk below is written for 256
+    static_assert(TILE == 256 || (!ONE_ROW && TILE == 128), "tile of 256, or 128 with K rows");
+    constexpr int LOADS = TILE * CH / kIdxThreads;
+    __shared__ u32x4 lds[TILE * CH];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -115,8 +118,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     // tokens costs about one 32-token block and rides along with another
     // tile's workgroup (the interleave below hands it to one of them).
     auto tiles_of = [&](int lm) {
-        const int nt = (lm + kIdxTile - 1) / kIdxTile;
-        return (uint32_t)(nt > 1 && lm - (nt - 1) * kIdxTile <= kIdxLightTail ? nt - 1 : nt);
+        const int nt = (lm + TILE - 1) / TILE;
+        return (uint32_t)(nt > 1 && lm - (nt - 1) * TILE <= kIdxLightTail ? nt - 1 : nt);
     };
     uint32_t my_tiles = 0;
     for (int sq = sq0; sq < sq1; sq++)
@@ -167,10 +170,10 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const int lmax = claim[3];
     // tiles interleave across the sequence's workgroups (workgroup x takes
     // tiles x, x + W, x + 2W, ...), so at any moment the workgroups stream
-    // neighbouring 64 KiB blocks and spread over every HBM channel
+    // neighbouring tiles and spread over every HBM channel
     const int W = claim[2];
     const int tile_first = claim[1];
-    const int tile_end = (lmax + kIdxTile - 1) / kIdxTile;
+    const int tile_end = (lmax + TILE - 1) / TILE;
     if (tile_first >= tile_end)
         return;
 
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     // i * kIdxThreads + tid of the tile, i.e. row g / CH, chunk g % CH
     auto load_part = [&](int tile, auto i0c, auto i1c) {
         constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
-        const int tile_bytes = tile * kIdxTile * D * 2;
+        const int tile_bytes = tile * TILE * D * 2;
 #pragma unroll
         for (int i = I0; i < I1; i++)
             regs[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, tile_bytes + (i * kIdxThreads + tid) * 16,
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     // into four contiguous ranges, one per wave, in row-major order, so a
     // wave keeps one row's query across blocks (with K = 4 each wave owns
     // one row for the whole run and loads its query once).
-    constexpr int kBlocks = kIdxTile / 32;
+    constexpr int kBlocks = TILE / 32;
     const int items = K * kBlocks / (kIdxThreads / kWave);
     const int item0 = wave * items;
     // The first tile's key loads go out before the query's: the query is
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         load_row(s * K + loaded);
     }
     for (int tile = tile_first; tile < tile_end; tile += W) {
-        const int t0 = tile * kIdxTile;
+        const int t0 = tile * TILE;
         const bool more = tile + W < tile_end;
         __syncthreads(); // every wave is done reading the previous tile
         // park the tile in LDS half by half; each half's registers take the
@@ -347,17 +350,27 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     }
 }
 
-template <int D, bool ONE_ROW, bool GM>
+template <int D, bool ONE_ROW, bool GM, int TILE = kIdxTile>
 static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
                        const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
                        uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t)
 {
-    hipExtLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM>), grid, dim3(kIdxThreads), 0, stream,
+    hipExtLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM, TILE>), grid, dim3(kIdxThreads), 0, stream,
                           t.start, t.stop, 0u,
                        q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.num_seqs,
                        ls.rows_per_seq,
                        ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls));
 }
+
+// Tokens per tile of the K-row pass. With two or four rows every wave owns
+// whole rows, and 128-token tiles give each workgroup twice as many steps of
+// its load/compute pipeline (four instead of two at the 16 x 4 verify shape:
+// 25.7 -> 23.3 us measured); the first tile's wait and the last tile's
+// compute, which nothing overlaps, are then half as long. With more rows a
+// wave walks several rows per tile and reloads their queries per tile, and
+// 256-token tiles stay faster (16 rows: 28.9 against 35.5 us). The pair walk
+// needs an even item count per wave, so odd K keeps 256 as well.
+static int rows_tile(int K) { return K == 2 || K == 4 ? 128 : kIdxTile; }
 
 template <int D>
 static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
@@ -366,12 +379,19 @@ static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, co
 {
     const bool one = ls.rows_per_seq == 1;
     const bool gm = gm4 != nullptr;
+    const bool half = rows_tile(ls.rows_per_seq) == 128;
     if (one && gm)
         launch_one<D, true, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                   stream, t);
     else if (one)
         launch_one<D, true, false>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                    stream, t);
+    else if (gm && half)
+        launch_one<D, false, true, 128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
+                                        stream, t);
+    else if (half)
+        launch_one<D, false, false, 128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4,
+                                         gm32, stream, t);
     else if (gm)
         launch_one<D, false, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                    stream, t);
