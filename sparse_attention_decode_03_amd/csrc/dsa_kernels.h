@@ -37,8 +37,8 @@ constexpr int kAttHeads = 64;
 inline int score_stride(const LaunchShape &ls) { return (ls.max_len + 63) / 64 * 64; }
 
 // Index-score pass geometry: 256-token tiles, 128 for two or four rows per
-// sequence (the balance of tiles over workgroups is computed on the device
-// from the lengths).
+// sequence and for calls with few tiles (the balance of tiles over
+// workgroups is computed on the device from the lengths).
 constexpr int kIdxTile = 256;
 // A last tile this short does not count as a tile of work in the split.
 constexpr int kIdxLightTail = 32;

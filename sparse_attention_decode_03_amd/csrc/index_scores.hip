@@ -8,8 +8,9 @@
 //
 // Design (HBM-bound: 256 B of keys per token at D = 128 against 8 kflop):
 //  - One workgroup walks every W-th tile of one sequence (256 tokens; 128
-//    when two or four rows share the keys) and scores each tile for every
-//    row of that sequence (the K rows of a verify share one key read). Keys stream HBM -> VGPR with fully coalesced 16-byte
+//    when two or four rows share the keys, or when the call has too few
+//    tiles to give each workgroup more than one) and scores each tile for
+//    every row of that sequence (the K rows of a verify share one key read). Keys stream HBM -> VGPR with fully coalesced 16-byte
 //    loads (the next tile's loads are in flight while the current tile
 //    computes) and are parked in LDS with an XOR swizzle, then re-read in
 //    matrix-core operand order without bank conflicts.
@@ -84,9 +85,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
 {
     constexpr int CH = D / 8;  // 16-byte chunks per key row
     constexpr int KS = D / 16; // MFMA k-steps
-    // TILE tokens per tile: 256 with one row, 128 or 256 with K rows (see
-    // rows_tile); the single-row walk below is written for 256
-    static_assert(TILE == 256 || (!ONE_ROW && TILE == 128), "tile of 256, or 128 with K rows");
+    // TILE tokens per tile: 256 or 128 (see rows_tile and row_tile)
+    static_assert(TILE == 256 || TILE == 128, "tiles of 256 or 128 tokens");
     constexpr int LOADS = TILE * CH / kIdxThreads;
     __shared__ u32x4 lds[TILE * CH];
 
@@ -313,11 +313,14 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         __syncthreads();
 
         if (ONE_ROW) {
-            // key operands: column (token) lane%32, k-chunks hl*KS + ks
-            bf16x8 kb[2][KS];
+            // wave w scores tokens [w TILE / 4, (w + 1) TILE / 4) of the tile:
+            // NB 32-token blocks; key operands: column (token) lane%32,
+            // k-chunks hl*KS + ks
+            constexpr int NB = TILE / 128;
+            bf16x8 kb[NB][KS];
 #pragma unroll
-            for (int b = 0; b < 2; b++) {
-                const int row = wave * 64 + b * 32 + (lane & 31);
+            for (int b = 0; b < NB; b++) {
+                const int row = wave * (TILE / 4) + b * 32 + (lane & 31);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
                     const int c = hl * KS + ks;
@@ -325,8 +328,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                 }
             }
 #pragma unroll
-            for (int b = 0; b < 2; b++)
-                score_block(s, lmax, t0, wave * 64 + b * 32, kb[b]);
+            for (int b = 0; b < NB; b++)
+                score_block(s, lmax, t0, wave * (TILE / 4) + b * 32, kb[b]);
         } else {
             // the wave's (row, 32-token block) items, two at a time: a range
             // starts at an even item and the blocks per row are even, so a
@@ -371,6 +374,15 @@ static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, 
 // 256-token tiles stay faster (16 rows: 28.9 against 35.5 us). The pair walk
 // needs an even item count per wave, so odd K keeps 256 as well.
 static int rows_tile(int K) { return K == 2 || K == 4 ? 128 : kIdxTile; }
+// Tokens per tile of the single-row pass. When even rows of max_len tokens
+// would give each workgroup at most one 256-token tile, 128-token tiles
+// double the workgroups that share the row and halve each one's serial
+// load-then-compute (1 x 8192: 6.2 -> 5.4 us measured); with more tiles than
+// workgroups, 256 is faster (8 x 131072: 45.9 against 49.5 us).
+static int row_tile(const LaunchShape &ls)
+{
+    return (int64_t)ls.num_seqs * ((ls.max_len + kIdxTile - 1) / kIdxTile) <= kIdxWgTarget ? 128 : kIdxTile;
+}
 
 template <int D>
 static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
@@ -379,8 +391,14 @@ static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, co
 {
     const bool one = ls.rows_per_seq == 1;
     const bool gm = gm4 != nullptr;
-    const bool half = rows_tile(ls.rows_per_seq) == 128;
-    if (one && gm)
+    const bool half = one ? row_tile(ls) == 128 : rows_tile(ls.rows_per_seq) == 128;
+    if (one && gm && half)
+        launch_one<D, true, true, 128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
+                                       stream, t);
+    else if (one && half)
+        launch_one<D, true, false, 128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
+                                        stream, t);
+    else if (one && gm)
         launch_one<D, true, true>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                   stream, t);
     else if (one)

@@ -43,6 +43,10 @@ def test_tiny_workload_end_to_end():
     dict(num_seqs=2, rows_per_seq=2, lengths="ragged", lo=100, hi=1500, top_k=2048, seed=14,
          index_heads=4, index_dim=64, num_heads=8),
     dict(num_seqs=1, rows_per_seq=1, context=6000, top_k=2048, seed=15, key_dist="student_t3"),
+    # 128-token tiles of the K-row pass: four rows (direct selection), and
+    # two rows past 8192 tokens (group maxima for the threshold filter)
+    dict(num_seqs=3, rows_per_seq=4, lengths="verify", base=3000, top_k=512, seed=16),
+    dict(num_seqs=2, rows_per_seq=2, lengths="verify", base=9500, top_k=1024, seed=17),
 ])
 def test_parity_across_tiles_chunks_and_tails(case):
     full_check(small(**case))
