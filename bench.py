@@ -59,14 +59,17 @@ def kernel_sha() -> str:
     return hashlib.sha256(open(INDEX_SRC, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic():
+def load_traffic(workload: str):
     """HBM bytes per index-kernel launch from the committed rocprofv3 counter
-    runs, only while the kernel source still matches the one measured."""
+    runs: only for the workload they were taken on, and only while the kernel
+    source still matches the one measured."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_sha") != kernel_sha():
+        return None
+    if rec.get("workload", "").split(":")[0].strip() != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -297,7 +300,7 @@ def main() -> int:
     ms = elapsed / args.steps * 1e3
     idx_us = stage_us["index"]
     achieved = ab["index"] / (idx_us * 1e-6) / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic(wlk.name)
     # the indexer plus the gather-attend (attention and chunk merge), against
     # every algorithmic byte of the step (keys, selected rows, q/out,
     # q_idx/w, block-table entries)
@@ -325,7 +328,8 @@ def main() -> int:
             "parallelism": "single-gpu", "replicas": nrep,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "k_index_scores (in-step: scores and group maxima)",
+            "bound": "hbm",
+            "kernel": "k_index_scores (in-step: scores" + (" and group maxima)" if int(inputs["max_len"]) > dsa.SELECT_DIRECT_MAX else ")"),
             "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,

@@ -1,10 +1,13 @@
 """CPU checks of bench.py's accounting: the algorithmic bytes its roofline
-figures divide by, and its refusal of more than one GPU."""
+figures divide by, its refusal of more than one GPU, and which workload its counter
+record belongs to."""
+import json
 import os
 import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -48,3 +51,12 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_traffic_record_is_only_reported_for_its_own_workload():
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    if rec.get("kernel_sha") != bench.kernel_sha():
+        pytest.skip("the committed counter record predates the current index kernel")
+    assert bench.load_traffic("long") == rec["bytes_per_launch"]
+    for w in ("kverify", "batched", "single", "rowgroup", "tiny"):
+        assert bench.load_traffic(w) is None
