@@ -36,9 +36,9 @@ constexpr int kAttHeads = 64;
 // row starts 256-byte aligned.
 inline int score_stride(const LaunchShape &ls) { return (ls.max_len + 63) / 64 * 64; }
 
-// Index-score pass geometry: 256-token tiles, 128 for two or four rows per
-// sequence and for calls with few tiles (the balance of tiles over
-// workgroups is computed on the device from the lengths).
+// Index-score pass geometry: 256-token tiles, 128 for units of two or four
+// rows and for calls with few tiles (the balance of tiles over workgroups is
+// computed on the device from the lengths).
 constexpr int kIdxTile = 256;
 // A last tile this short does not count as a tile of work in the split.
 constexpr int kIdxLightTail = 32;

@@ -10,7 +10,9 @@
 //  - One workgroup walks every W-th tile of one sequence (256 tokens; 128
 //    when two or four rows share the keys, or when the call has too few
 //    tiles to give each workgroup more than one) and scores each tile for
-//    every row of that sequence (the K rows of a verify share one key read). Keys stream HBM -> VGPR with fully coalesced 16-byte
+//    the rows of its unit: all K rows of the sequence (the rows of a verify
+//    share one key read), or a group of four (or two) of them when K is
+//    larger, each group walking the keys on its own. Keys stream HBM -> VGPR with fully coalesced 16-byte
 //    loads (the next tile's loads are in flight while the current tile
 //    computes) and are parked in LDS with an XOR swizzle, then re-read in
 //    matrix-core operand order without bank conflicts.
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w,
     const uint16_t *__restrict__ k_normed, const int32_t *__restrict__ seq_lens,
     float *__restrict__ scores, uint32_t *__restrict__ gm4, uint32_t *__restrict__ gm32, int S,
-    int K, int Hi, int64_t cap, int max_len, int stride)
+    int K, int KG, int Hi, int64_t cap, int max_len, int stride)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per key row
     constexpr int KS = D / 16; // MFMA k-steps
@@ -95,24 +97,29 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave); // uniform: scalar row math
     const int hl = lane / 32;
 
-    // ---- balance the tiles of all sequences over about kIdxWgTarget
-    // workgroups from the device-side lengths: every workgroup computes the
-    // same split (tiles per workgroup from the total), sequence s gets
-    // ceil(tiles_s / tpw) workgroups, and this workgroup claims its sequence
-    // and slot from a prefix of those counts ----
+    // ---- balance the tiles of all units over about kIdxWgTarget workgroups
+    // from the device-side lengths. A unit is KG rows of one sequence (all
+    // K rows, or a group of them: unit u is rows KG (u mod RG) .. + KG - 1
+    // of sequence u / RG, RG = K / KG). Every workgroup computes the same
+    // split (tiles per workgroup from the total), unit u gets
+    // ceil(tiles_u / tpw) workgroups, and this workgroup claims its unit and
+    // slot from a prefix of those counts ----
     __shared__ uint32_t bscan[kIdxThreads / kWave + 1];
     __shared__ int claim[4];
-    __shared__ int s_len[kMaxRowsPerSeq]; // lengths of the claimed sequence's rows
+    __shared__ int s_len[kMaxRowsPerSeq]; // lengths of the claimed unit's rows
+    const int RG = K / KG;                // units per sequence
+    const int SU = S * RG;                // units
     auto row_len = [&](int r) { return min(max(seq_lens[r], 0), max_len); };
-    auto seq_lmax = [&](int sq) {
+    auto unit_row = [&](int u) { return (u / RG) * K + (u % RG) * KG; }; // the unit's first row
+    auto seq_lmax = [&](int u) {
         int lm = 0;
-        for (int j = 0; j < K; j++)
-            lm = max(lm, row_len(sq * K + j));
+        for (int j = 0; j < KG; j++)
+            lm = max(lm, row_len(unit_row(u) + j));
         return lm;
     };
-    const int per = (S + kIdxThreads - 1) / kIdxThreads; // sequences per thread
-    const int sq0 = min(tid * per, S), sq1 = min(sq0 + per, S);
-    // the first sequence's length is kept (the only one up to 256 sequences)
+    const int per = (SU + kIdxThreads - 1) / kIdxThreads; // units per thread
+    const int sq0 = min(tid * per, SU), sq1 = min(sq0 + per, SU);
+    // the first unit's length is kept (the only one up to 256 units)
     const int lm0 = sq0 < sq1 ? seq_lmax(sq0) : 0;
     // Tiles that count for the split: a last tile of at most kIdxLightTail
     // tokens costs about one 32-token block and rides along with another
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     // Tiles per workgroup: the smallest count from ceil(total / target) up
     // whose split needs at most kIdxWgTarget workgroups (two per CU, all
     // resident at once), tried a few times; any count from the first on
-    // needs at most kIdxWgTarget + S workgroups, the grid.
+    // needs at most kIdxWgTarget + SU workgroups, the grid.
     uint32_t tpw = max(1u, (total_tiles + kIdxWgTarget - 1) / kIdxWgTarget);
     uint32_t my_wgs, wg_base, total_wgs;
     for (int attempt = 0;; attempt++, tpw++) {
@@ -154,8 +161,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                 claim[1] = (int)(me - at);
                 claim[2] = (int)w_s;
                 claim[3] = lm;
-                for (int j = 0; j < K; j++)
-                    s_len[j] = row_len(sq * K + j);
+                for (int j = 0; j < KG; j++)
+                    s_len[j] = row_len(unit_row(sq) + j);
                 break;
             }
             at += w_s;
@@ -164,8 +171,9 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     __syncthreads();
     if (claim[0] < 0)
         return; // past the last workgroup this split needs
-    const int s = claim[0];
-    // the longest row of the sequence: the tiles to score (from the claim, so
+    const int s = claim[0] / RG;          // the unit's sequence
+    const int rbase = unit_row(claim[0]); // and its first row
+    // the longest row of the unit: the tiles to score (from the claim, so
     // the first tile's loads go out with no further length load)
     const int lmax = claim[3];
     // tiles interleave across the sequence's workgroups (workgroup x takes
@@ -279,12 +287,12 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         block_out(r, L, t0, col0 + 32, acc[1]);
     };
 
-    // Several rows (K > 1): the tile's K x 8 (row, block) items are split
-    // into four contiguous ranges, one per wave, in row-major order, so a
-    // wave keeps one row's query across blocks (with K = 4 each wave owns
-    // one row for the whole run and loads its query once).
+    // Several rows (KG > 1): the tile's KG x (TILE / 32) (row, block) items
+    // are split into four contiguous ranges, one per wave, in row-major
+    // order, so a wave keeps one row's query across blocks (with KG = 4 each
+    // wave owns one row for the whole run and loads its query once).
     constexpr int kBlocks = TILE / 32;
-    const int items = K * kBlocks / (kIdxThreads / kWave);
+    const int items = KG * kBlocks / (kIdxThreads / kWave);
     const int item0 = wave * items;
     // The first tile's key loads go out before the query's: the query is
     // used (padding heads zeroed) as soon as it lands, and loads issued
@@ -292,10 +300,10 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     load_part(tile_first, IC0{}, ICL{});
     int loaded = -1;
     if (ONE_ROW) {
-        load_row(s);
+        load_row(rbase);
     } else if (item0 / kBlocks == (item0 + items - 1) / kBlocks) {
         loaded = item0 / kBlocks;
-        load_row(s * K + loaded);
+        load_row(rbase + loaded);
     }
     for (int tile = tile_first; tile < tile_end; tile += W) {
         const int t0 = tile * TILE;
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
             }
 #pragma unroll
             for (int b = 0; b < NB; b++)
-                score_block(s, lmax, t0, wave * (TILE / 4) + b * 32, kb[b]);
+                score_block(rbase, lmax, t0, wave * (TILE / 4) + b * 32, kb[b]);
         } else {
             // the wave's (row, 32-token block) items, two at a time: a range
             // starts at an even item and the blocks per row are even, so a
@@ -339,7 +347,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
             for (int it = item0; it < item0 + items; it += 2) {
                 const int j = it / kBlocks;
                 const int blk = it % kBlocks;
-                const int r = s * K + j;
+                const int r = rbase + j;
                 const int L = s_len[j]; // from LDS: no wait on the loads in flight
                 if (t0 + blk * 32 >= L)
                     continue;
@@ -353,6 +361,15 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
     }
 }
 
+// Rows per unit of the K-row pass: K rows of a sequence are scored as K / KG
+// units of KG rows, each walking the sequence's keys on its own (KG = 4 when
+// K is a multiple of 4, else 2 when K is even, else K). A unit of four rows
+// is the shape where every wave owns one row. 16 rows in one unit left each
+// wave four rows and each workgroup a single 256-token tile (8 x 16 rows at
+// ~9k tokens: 29.5 us; units of eight rows 34.4 us; of four 25.4 us, for
+// four times the key reads).
+static int rows_group(int K) { return K % 4 == 0 ? 4 : K % 2 == 0 ? 2 : K; }
+
 template <int D, bool ONE_ROW, bool GM, int TILE = kIdxTile>
 static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, const float *w,
                        const uint16_t *k_normed, const int32_t *seq_lens, float *scores,
@@ -361,19 +378,18 @@ static void launch_one(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, 
     hipExtLaunchKernelGGL((k_index_scores<D, ONE_ROW, GM, TILE>), grid, dim3(kIdxThreads), 0, stream,
                           t.start, t.stop, 0u,
                        q_idx, w, k_normed, seq_lens, scores, gm4, gm32, ls.num_seqs,
-                       ls.rows_per_seq,
+                       ls.rows_per_seq, rows_group(ls.rows_per_seq),
                        ls.index_heads, (int64_t)ls.k_capacity, ls.max_len, score_stride(ls));
 }
 
-// Tokens per tile of the K-row pass. With two or four rows every wave owns
-// whole rows, and 128-token tiles give each workgroup twice as many steps of
-// its load/compute pipeline (four instead of two at the 16 x 4 verify shape:
-// 25.7 -> 23.3 us measured); the first tile's wait and the last tile's
-// compute, which nothing overlaps, are then half as long. With more rows a
-// wave walks several rows per tile and reloads their queries per tile, and
-// 256-token tiles stay faster (16 rows: 28.9 against 35.5 us). The pair walk
-// needs an even item count per wave, so odd K keeps 256 as well.
-static int rows_tile(int K) { return K == 2 || K == 4 ? 128 : kIdxTile; }
+// Tokens per tile of the K-row pass, by rows per unit. With two or four
+// rows every wave owns whole rows, and 128-token tiles give each workgroup
+// twice as many steps of its load/compute pipeline (four instead of two at
+// the 16 x 4 verify shape: 25.7 -> 23.3 us measured); the first tile's wait
+// and the last tile's compute, which nothing overlaps, are then half as
+// long. The pair walk needs an even item count per wave, so an odd unit
+// keeps 256.
+static int rows_tile(int KG) { return KG == 2 || KG == 4 ? 128 : kIdxTile; }
 // Tokens per tile of the single-row pass. When even rows of max_len tokens
 // would give each workgroup at most one 256-token tile, 128-token tiles
 // double the workgroups that share the row and halve each one's serial
@@ -391,7 +407,7 @@ static void launch_d(const LaunchShape &ls, dim3 grid, const uint16_t *q_idx, co
 {
     const bool one = ls.rows_per_seq == 1;
     const bool gm = gm4 != nullptr;
-    const bool half = one ? row_tile(ls) == 128 : rows_tile(ls.rows_per_seq) == 128;
+    const bool half = one ? row_tile(ls) == 128 : rows_tile(rows_group(ls.rows_per_seq)) == 128;
     if (one && gm && half)
         launch_one<D, true, true, 128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32,
                                        stream, t);
@@ -427,7 +443,8 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
     // About kIdxWgTarget workgroups in all, balanced over the sequences by
     // their device-side lengths; each walks every W-th tile of one sequence
     // with the next tile's loads in flight.
-    dim3 grid(kIdxWgTarget + ls.num_seqs); // enough for any split of the tiles
+    // enough for any split of the tiles over the units
+    dim3 grid(kIdxWgTarget + ls.num_seqs * (ls.rows_per_seq / rows_group(ls.rows_per_seq)));
     if (ls.index_dim == 128)
         launch_d<128>(ls, grid, q_idx, w, k_normed, seq_lens, scores, gm4, gm32, stream, t);
     else if (ls.index_dim == 64)

@@ -47,6 +47,8 @@ def test_tiny_workload_end_to_end():
     # two rows past 8192 tokens (group maxima for the threshold filter)
     dict(num_seqs=3, rows_per_seq=4, lengths="verify", base=3000, top_k=512, seed=16),
     dict(num_seqs=2, rows_per_seq=2, lengths="verify", base=9500, top_k=1024, seed=17),
+    # six rows: three units of two rows per sequence, each walking the keys
+    dict(num_seqs=2, rows_per_seq=6, lengths="verify", base=4000, top_k=512, seed=18),
 ])
 def test_parity_across_tiles_chunks_and_tails(case):
     full_check(small(**case))
