@@ -300,26 +300,50 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     // ================= phase 2: QK and the chunk's maxima =================
     // lane: head hl, tokens 16 tt + 4 g + v of each of its token tiles
     floatx4 z[kTpw];
+    // The FP8 operands of four k-steps of a tile pair (tiles tt, tt + 1, the
+    // two halves of step tt / 2); the next group's are requested before this
+    // group's conversions and products, so the LDS reads stay in flight
+    // behind them.
+    auto qk_operands = [&](int j, int k0, v2i (&a)[2][4]) {
+        const uint8_t *tb = ring + ((tt0 + j) >> 1) * kTileBytes;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int chunk = 2 * (k0 + k) + (g >> 1);
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+                a[h][k] = *(const v2i *)(tb + tile_off(16 * h + n16, chunk) + 8 * (g & 1));
+        }
+    };
+    // (with 64 heads the registers this takes cost more than it saves:
+    // measured, so that form requests each group's operands in turn)
+    constexpr bool kPf = kHt < 4;
+    v2i a[2][4];
+    if (kPf)
+        qk_operands(0, 0, a);
 #pragma unroll
     for (int j = 0; j < kTpw; j += 2) {
         floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
         const int tt = tt0 + j; // even: tiles tt, tt + 1 are the two halves of step tt / 2
-        const uint8_t *tb = ring + (tt >> 1) * kTileBytes;
 #pragma unroll
         for (int k0 = 0; k0 < 16; k0 += 4) {
-            v2i a[2][4];
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const int chunk = 2 * (k0 + k) + (g >> 1);
-#pragma unroll
-                for (int h = 0; h < 2; h++)
-                    a[h][k] = *(const v2i *)(tb + tile_off(16 * h + n16, chunk) + 8 * (g & 1));
-            }
+            if (!kPf)
+                qk_operands(j, k0, a);
+            v2i an[2][4];
+            const int nj = k0 == 12 ? j + 2 : j;
+            if (kPf && nj < kTpw)
+                qk_operands(nj, k0 == 12 ? 0 : k0 + 4, an);
 #pragma unroll
             for (int k = 0; k < 4; k++) {
 #pragma unroll
                 for (int h = 0; h < 2; h++)
                     acc[h] = mfma16x16x32(fp8x8_to_bf16x8(a[h][k]), as_bf16x8(qr[k0 + k]), acc[h]);
+            }
+            if (kPf && nj < kTpw) {
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+                        a[h][k] = an[h][k];
             }
         }
 #pragma unroll
