@@ -4,9 +4,10 @@ oracle's full sort under (score descending, index ascending).
 
 The model follows the kernels step by step: the threshold tau from the
 largest key of each 4-token or 32-token group (one 12-bit digit relative to
-the group keys' range), the candidates {key >= tau}, then the exact cut --
-relative 12-bit digits narrow a key window onto the bin holding the
-top_k-th candidate, and that bin's members are ranked directly. It exists to
+the group keys' range), the candidates {key >= tau}, then the exact cut -- relative 12-bit
+digits narrow a key window onto the bin holding the top_k-th candidate
+(after a first pass of value-linear bins when the candidates lie on both
+sides of zero), and that bin's members are ranked directly. It exists to
 show, on the CPU, that the crafted rows of the GPU route tests really reach
 the narrowing route (a boundary bin of more than 256 members whose window is
 then narrower than 12 bits), and that counting only the keys inside the
@@ -36,6 +37,29 @@ def order_keys(scores: np.ndarray) -> np.ndarray:
 
 def bit_len(x: int) -> int:
     return int(x).bit_length()
+
+
+def key_values(keys: np.ndarray) -> np.ndarray:
+    """fp32 values of order keys (the inverse of order_keys)."""
+    k = keys.astype(np.uint32)
+    u = np.where((k & 0x80000000) != 0, k & np.uint32(0x7FFFFFFF), ~k).astype(np.uint32)
+    return u.view(np.float32)
+
+
+def value_bins(keys: np.ndarray, lo: int, hi: int):
+    """The kernels' value-linear bins in fp32, or None when the key range
+    [lo, hi] does not straddle zero (or its value span is not finite):
+    bin = min(4095, floor((value - value(lo)) * (4096 / span)))."""
+    if not (lo < 0x80000000 <= hi):
+        return None
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        vlo = key_values(np.array([lo], np.uint32))[0]
+        span = np.float32(key_values(np.array([hi], np.uint32))[0] - vlo)
+        scale = np.float32(np.float32(BINS) / span)
+        if not (span > 0 and np.isfinite(span) and np.isfinite(scale)):
+            return None
+        x = np.float32(key_values(keys) - vlo) * scale
+    return np.minimum(x.astype(np.float32), np.float32(BINS - 1)).astype(np.int64)
 
 
 def walk_desc(hist: np.ndarray, need: int):
@@ -82,15 +106,32 @@ def exact_cut(kk: np.ndarray, ids: np.ndarray, top_k: int, window_only: bool = T
     a narrowed window was below 12 bits, and how the boundary bin was ranked
     ('member list' for at most 256 members, 'equal keys' by index otherwise)."""
     kk = kk.astype(np.int64)
-    base = int(kk.min())
-    bits = bit_len(int(kk.max()) - base)
     need = top_k
     passes = 0
     narrow = False
+    pre = np.zeros(len(kk), bool)     # taken by the value pass
+    valid = np.ones(len(kk), bool)
+    vb = value_bins(kk.astype(np.uint32), int(kk.min()), int(kk.max()))
+    if vb is not None:
+        b, before, total = walk_desc(np.bincount(vb, minlength=BINS), need)
+        passes += 1
+        assert total >= top_k
+        need -= before
+        pre = vb > b
+        valid = vb == b
+        if valid.sum() <= RANK_LIST:
+            members = np.flatnonzero(valid)
+            order = sorted(members, key=lambda j: (-kk[j], ids[j]))
+            take = pre.copy()
+            take[np.array(order[:max(need, 0)], dtype=np.int64)] = True
+            return np.sort(ids[take]), dict(passes=passes, narrow=narrow, rank="member list",
+                                            value_pass=True)
+    base = int(kk[valid].min())
+    bits = bit_len(int(kk[valid].max()) - base)
     while True:
         shift = max(bits - DIGIT, 0)
         nb = 1 << (bits - shift) if window_only else BINS
-        inside = kk >= base
+        inside = valid & (kk >= base)
         d = (kk - base) >> shift
         inside &= d < nb
         hist = np.bincount(d[inside], minlength=BINS)
@@ -105,13 +146,14 @@ def exact_cut(kk: np.ndarray, ids: np.ndarray, top_k: int, window_only: bool = T
             break
         base, bits = bin_lo, shift
         narrow |= bits < DIGIT
-    take = kk >= bin_lo + (1 << shift)
-    inbin = (kk >= bin_lo) & ~take
+    take = valid & (kk >= bin_lo + (1 << shift))
+    inbin = valid & (kk >= bin_lo) & ~take
+    take |= pre
     members = np.flatnonzero(inbin)
     order = sorted(members, key=lambda j: (-kk[j], ids[j]))
     take[np.array(order[:max(need, 0)], dtype=np.int64)] = True
     rank = "member list" if count_b <= RANK_LIST else "equal keys"
-    return np.sort(ids[take]), dict(passes=passes, narrow=narrow, rank=rank)
+    return np.sort(ids[take]), dict(passes=passes, narrow=narrow, rank=rank, value_pass=vb is not None)
 
 
 def gather_mode(cand: np.ndarray, L: int) -> str:
@@ -194,6 +236,8 @@ def test_gpu_route_rows_cover_every_route():
             seen.add(info["route"])
             if info["route"] == "cut":
                 seen.update({info["level"], info["gather"], info["rank"]})
+                if info["value_pass"]:
+                    seen.add("value-bin first cut pass")
                 if info["passes"] >= 2:
                     seen.add("narrowed" + (" below 12 bits" if info["narrow"] else ""))
                 if max_len == 131072 and top_k == 2048:
@@ -201,5 +245,6 @@ def test_gpu_route_rows_cover_every_route():
             elif info["route"] == "full":
                 seen.add(info["level"])
     want = {"all", "full", "cut", "gm4 registers", "gm4 memory", "gm32", "every token",
-            "by slice", "spread", "member list", "equal keys", "narrowed below 12 bits"}
+            "by slice", "spread", "member list", "equal keys", "narrowed below 12 bits",
+            "value-bin first cut pass"}
     assert want <= seen, f"routes not reached: {sorted(want - seen)}"
