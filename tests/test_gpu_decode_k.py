@@ -46,7 +46,10 @@ def assert_serial_equals_batched(inputs):
             assert np.array_equal(ou[i], b_out[r]), r
 
 
-@pytest.mark.parametrize("K,seed", [(2, 1), (4, 2), (8, 3)])
+# K = 2 and 4: one unit of rows per sequence in the index pass (128-token
+# tiles); 6, 8 and 12: units of two or four rows each walking the keys; 3:
+# one odd unit (256-token tiles)
+@pytest.mark.parametrize("K,seed", [(2, 1), (4, 2), (8, 3), (3, 4), (6, 5), (12, 6)])
 def test_verify_rows_bit_identical_to_serial_calls(K, seed):
     # The K-row call has more (row, chunk) work than each serial call, so
     # the attention runs in larger head groups: 16 heads for the serial
