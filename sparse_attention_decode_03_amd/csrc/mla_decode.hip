@@ -500,6 +500,465 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     }
 }
 
+// ---------------------------------------------------------------------------
+// More (row, chunk) units of 64 heads than CUs: one workgroup per CU takes a
+// run of consecutive units in turn (chunks of one row, mostly: the query
+// stays in registers), so that the ring never idles between units. While
+// unit u runs its softmax and P.V, the next unit's length and selected ids
+// are requested, and its tile copies go out as P.V frees the ring (steps 0-3
+// after the first P.V pass, 4-7 after the second); its QK then runs over step
+// pairs as they land, and unit u's output is stored during that QK. QK ownership: wave w scores token tile
+// 2 st + (w & 1) of every step st for head tile w >> 1 (two waves a head
+// tile, as in k_mla_decode<64>). Every element's arithmetic is k_mla_decode's
+// (the same MFMA chains, maxima, exponentials, tile sums, P rounding and P.V
+// step order), so a row's output has the same bits from either kernel.
+//
+// The pointers carry no __restrict__: loads through const restrict pointers
+// count as invariant, and the next unit's query and id loads must stay where
+// they are issued rather than sink to their use.
+constexpr int kWaitVmLgkm0 = 0x0070; // s_waitcnt vmcnt(0) lgkmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt lgkmcnt(0)
+
+// The thread id through an opaque move: lane-derived addresses computed from
+// it stay inside the unit loop instead of being hoisted out of it (with every
+// LDS and global address of a unit held in registers, the kernel spills).
+__device__ __forceinline__ int opaque_tid()
+{
+    int t;
+    __asm__ volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+    return t;
+}
+
+// The 4 x 4 transpose of 16-lane rows and four registers: on return, row g
+// of r[j] holds what row j of r[g] held (gfx950 lane swaps: the 32-lane swap
+// exchanges rows 2-3 of its first operand with rows 0-1 of its second, the
+// 16-lane swap rows 1 and 3 of its first with rows 0 and 2 of its second).
+__device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
+{
+    auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+    auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+    auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    r[0] = s01[0];
+    r[1] = s01[1];
+    r[2] = s23[0];
+    r[3] = s23[1];
+}
+
+// A workgroup barrier that publishes this wave's LDS writes but does not wait
+// for its vector-memory operations (tile copies stay in flight across it).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
+    const uint16_t *q, const uint8_t *kv, const int32_t *bt, const int32_t *seq_lens,
+    const int32_t *sel, uint16_t *part_o, float2 *part_ml, uint16_t *out, int K, int H, int top_k,
+    int ps, int max_blocks, int num_pages, int max_len, float kv_scale, float qk_log2, int nch_max,
+    int hg_count, int units)
+{
+    constexpr int G = kAttHeads;
+    constexpr int kHt = G / 16;                  // 4 head tiles
+    constexpr int kPTok = p_tokens<G>();         // P of 128 tokens in LDS at once
+    constexpr int kPRowBytes = p_row_bytes<G>();
+    constexpr int kStepsPerPass = kPTok / kStep; // 4
+    static_assert(kAttWaves == 2 * kHt && kMaxSteps == 8 && kStepsPerPass == 4,
+                  "two waves a head tile; eight steps, P.V in two passes of four");
+    __shared__ __align__(16) uint8_t ring[kMaxSteps * kTileBytes]; // FP8 step tiles (128 KiB)
+    __shared__ __align__(16) uint8_t pbuf[G * kPRowBytes];        // bf16 P of one pass
+    __shared__ float wmax[kAttWaves][16];
+    __shared__ float tsum[kTokTiles][G];
+    __shared__ __align__(16) uint8_t vmask[kAttChunk];
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int ht = wave >> 1;  // QK head tile
+    const int par = wave & 1;  // QK token tile 2 st + par of step st
+    const int per_row = hg_count * nch_max;
+    // this workgroup's units: [ubeg, uend)
+    const int upw = (units + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int ubeg = (int)blockIdx.x * upw;
+    const int uend = min(ubeg + upw, units);
+    // lane-derived values, recomputed where they are used
+#define PIPE_LANE                                                                              \
+    const int tid = opaque_tid();                                                              \
+    const int lane = tid % kWave;                                                              \
+    const int g = lane >> 4;                                                                   \
+    const int n16 = lane & 15;                                                                 \
+    const int slot = kStep * wave + (lane & 31); /* wave w copies step w of every unit */      \
+    const int hl = ht * 16 + n16;                /* this lane's QK head within the group */    \
+    (void)g;                                                                                   \
+    (void)slot;                                                                                \
+    (void)hl;
+
+    // ---- the unit being prepared (uniform but for the lane's id and page) ----
+    int nu = units, nr = 0, nhg = 0, nc = 0, nlen = 0, nnch = 0;
+    int t_seln = 0, pagen = -1;
+    auto issue_len = [&](int u) { // length and this lane's selected id of unit u
+        PIPE_LANE
+        nu = u;
+        nr = u / per_row;
+        const int rem = u - nr * per_row;
+        nhg = rem / nch_max;
+        nc = rem - nhg * nch_max;
+        nlen = seq_lens[nr];
+        t_seln = sel[(int64_t)nr * top_k + min(nc * kAttChunk + slot, top_k - 1)];
+    };
+    auto issue_q = [&](u32x4(&qd)[16]) { // the prepared unit's query (head tile ht)
+        PIPE_LANE
+        const uint16_t *qrow = q + ((int64_t)nr * H + min(nhg * G + hl, H - 1)) * kLat + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++)
+            qd[ks] = *(const u32x4 *)(qrow + 32 * ks);
+    };
+    // Settles the unit issue_a requested: an empty one (a row with nothing
+    // selected, or a chunk past the row's selection) is skipped, the first
+    // chunk of an empty row writing zeros, and the next candidate requested
+    // in its place. Returns whether a unit with work is prepared; its lane's
+    // page lookup is then in flight.
+    auto finish_b = [&]() -> bool {
+        PIPE_LANE
+        while (nu < units) {
+            const int L = min(max(__builtin_amdgcn_readfirstlane(nlen), 0), max_len);
+            const int n = min(top_k, L);
+            const int nch = (n + kAttChunk - 1) / kAttChunk;
+            if (n > 0 && nc < nch) {
+                const int nslots = min(n - nc * kAttChunk, kAttChunk);
+                nnch = nch;
+                pagen = -1;
+                if (slot < nslots && t_seln >= 0 && t_seln < L)
+                    pagen = bt[(int64_t)(nr / K) * max_blocks + t_seln / ps];
+                return true;
+            }
+            if (n == 0 && nc == 0) {
+                const int h0 = nhg * G;
+                for (int i = tid; i < G * kLat; i += kAttThreads) {
+                    const int h = h0 + i / kLat;
+                    if (h < H)
+                        out[((int64_t)nr * H + h) * kLat + (i % kLat)] = 0;
+                }
+            }
+            if (nu + 1 >= uend) {
+                nu = units;
+                break;
+            }
+            issue_len(nu + 1);
+        }
+        return false;
+    };
+    // Wave w's step of the prepared unit: masks, then the LDS-direct copies of
+    // its FP8 rows into ring slot w (a skipped slot copies one of the step's
+    // selected rows; a step with none is zeroed), as k_mla_decode does.
+    auto issue_tile = [&]() {
+        PIPE_LANE
+        const int row = (pagen >= 0 && pagen < num_pages) ? pagen * ps + t_seln % ps : -1;
+        if (lane < 32)
+            vmask[slot] = row >= 0 ? 1 : 0;
+        uint8_t *tile = ring + wave * kTileBytes;
+        const uint64_t any = __ballot(row >= 0) & 0xFFFFFFFFull;
+        if (any != 0) {
+            const int sub = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)any) - 1);
+            const int src = row >= 0 ? row : sub;
+            const int half = lane >> 5;
+#pragma unroll
+            for (int i = 0; i < kDmaPerStep; i++) {
+                const int rowa = __builtin_amdgcn_readlane(src, 2 * i);
+                const int rowb = __builtin_amdgcn_readlane(src, 2 * i + 1);
+                const int trow = 2 * i + half;
+                const int grow = half ? rowb : rowa;
+                const uint8_t *gsrc = kv + (int64_t)grow * kLat + 16 * ((lane & 31) ^ trow);
+                __builtin_amdgcn_global_load_lds((const void *)gsrc, (lds_void *)(tile + 2 * i * kLat),
+                                                 16, 0, 0);
+            }
+        } else {
+            for (int i = lane; i < kTileBytes / 16; i += kWave)
+                *(u32x4 *)(tile + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    // ---- the first unit ----
+    if (ubeg >= uend)
+        return;
+    issue_len(ubeg);
+    if (!finish_b())
+        return; // uniform: nothing to do
+    int cr = nr, chg = nhg, cc = nc, cnch = nnch, cu = nu;
+    issue_tile();
+    u32x4 qr[16];
+    issue_q(qr);
+    // (every load of the first unit retired here, so that no wait for the
+    // query lands inside the unit loop)
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+
+    // ---- the previous unit's output, stored after the next unit's QK ----
+    // (its O already rounded to bf16 as it is stored: scaled by kv_scale / l
+    // for a row of one chunk, unscaled as a chunk partial)
+    bool have_prev = false;
+    int pr = 0, phg = 0, pc = 0, pnch = 0;
+    float pm = 0.0f, plh = 0.0f; // (m, l) of head hl
+    u32x2 pw[kHt][kPvColTiles];
+#pragma unroll
+    for (int mt = 0; mt < kHt; mt++)
+#pragma unroll
+        for (int i = 0; i < kPvColTiles; i++)
+            pw[mt][i] = u32x2{0u, 0u};
+    auto store_prev = [&](int mt0, int mt1) { // head tiles mt0 .. mt1 - 1
+        PIPE_LANE
+        const int h0 = phg * G;
+        const int nh = min(G, H - h0);
+        const int64_t pb = (((int64_t)pr * hg_count + phg) * nch_max + pc) * G;
+        if (mt0 == 0 && pnch > 1 && par == 0 && g == 0 && hl < nh)
+            part_ml[pb + hl] = float2{pm, plh};
+        // Row g of column tile i holds columns 16 (4 w + i) + 4 g .. + 3 of
+        // head 16 mt + n16; after the transpose, row g holds the 16 columns
+        // 16 (4 w + g) .. + 15 (in four 8-byte pieces), so that the four rows
+        // fill whole 128-byte lines (8-byte pieces spread over lines leave
+        // them partly written, and the kernel's end waits for their
+        // write-back).
+#pragma unroll
+        for (int mt = 0; mt < kHt; mt++) {
+            if (mt < mt0 || mt >= mt1)
+                continue;
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int i = 0; i < kPvColTiles; i++) {
+                lo[i] = pw[mt][i].x;
+                hi[i] = pw[mt][i].y;
+            }
+            transpose_rows(lo);
+            transpose_rows(hi);
+            const int hrow = 16 * mt + n16;
+            const int col = 16 * (kPvColTiles * wave + g);
+            if (hrow < nh) {
+                const u32x4 v0 = u32x4{lo[0], hi[0], lo[1], hi[1]};
+                const u32x4 v1 = u32x4{lo[2], hi[2], lo[3], hi[3]};
+                if (pnch == 1) {
+                    uint16_t *orow = out + ((int64_t)pr * H + h0 + hrow) * kLat + col;
+                    *(u32x4 *)orow = v0;
+                    *(u32x4 *)(orow + 8) = v1;
+                } else {
+                    uint16_t *orow = part_o + (pb + hrow) * kLat + col;
+                    __builtin_nontemporal_store(v0, (u32x4 *)orow);
+                    __builtin_nontemporal_store(v1, (u32x4 *)(orow + 8));
+                }
+            }
+        }
+    };
+
+    for (;;) {
+        // ================= QK over step pairs as they land =================
+        floatx4 z[kMaxSteps]; // z[st]: token tile 2 st + par, head hl
+#pragma unroll
+        for (int p = 0; p < kMaxSteps / 2; p++) {
+            PIPE_LANE
+            if ((wave >> 1) == p) // waves 2p, 2p + 1 copied steps 2p, 2p + 1
+                __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+            __asm__ volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            __asm__ volatile("" ::: "memory");
+            // the previous unit's output, head tile mt stored in pair
+            // max(mt, w >> 1): never before this wave's own tile wait (a store
+            // issued earlier would hold that wait)
+            if (have_prev) {
+                const int q0 = wave >> 1;
+                if (p == q0)
+                    store_prev(0, p + 1);
+                else if (p > q0)
+                    store_prev(p, p + 1);
+            }
+            floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+            // the FP8 operands of four k-steps of both steps; the next group's
+            // are requested before this group's conversions and products
+            auto operands = [&](int k0, v2i(&a)[2][4]) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const uint8_t *tb = ring + (2 * p + h) * kTileBytes;
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        a[h][k] = *(const v2i *)(tb + tile_off(16 * par + n16, 2 * (k0 + k) + (g >> 1)) +
+                                                 8 * (g & 1));
+                }
+            };
+            v2i a[2][4];
+            operands(0, a);
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += 4) {
+                v2i an[2][4];
+                if (k0 < 12)
+                    operands(k0 + 4, an);
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+                        acc[h] = mfma16x16x32(fp8x8_to_bf16x8(a[h][k]), as_bf16x8(qr[k0 + k]), acc[h]);
+                if (k0 < 12) {
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+#pragma unroll
+                        for (int k = 0; k < 4; k++)
+                            a[h][k] = an[h][k];
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int tt = 2 * (2 * p + h) + par;
+                const uint32_t mw = *(const uint32_t *)(vmask + 16 * tt + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    z[2 * p + h][v] = ((mw >> (8 * v)) & 0xFFu) ? acc[h][v] * qk_log2 : kNegInf;
+            }
+        }
+
+        // ================= the next unit: length and ids =================
+        if (cu + 1 < uend)
+            issue_len(cu + 1);
+        else
+            nu = units;
+
+        // ================= maxima and softmax over the chunk =================
+        {
+            PIPE_LANE
+            float mx = kNegInf;
+#pragma unroll
+            for (int st = 0; st < kMaxSteps; st++)
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    mx = __builtin_fmaxf(mx, z[st][v]);
+            mx = max_xor32(max_xor16(mx));
+            if (g == 0)
+                wmax[wave][n16] = mx;
+        }
+        lds_barrier(); // wave maxima (every wave is past its QK: the vmask reads are done)
+        float m;
+        u32x2 pk[kMaxSteps];
+        {
+        PIPE_LANE
+        m = __builtin_fmaxf(wmax[2 * ht][n16], wmax[2 * ht + 1][n16]);
+        const float m_use = (m == kNegInf) ? 0.0f : m;
+#pragma unroll
+        for (int st = 0; st < kMaxSteps; st++) {
+            float p4[4];
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                p4[v] = exp2f(z[st][v] - m_use);
+            float ts = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+            ts = add_xor32(add_xor16(ts));
+            if (g == 0)
+                tsum[2 * st + par][hl] = ts;
+            pk[st].x = pack_bf16x2(p4[0], p4[1]);
+            pk[st].y = pack_bf16x2(p4[2], p4[3]);
+        }
+        }
+
+        // ================= P.V, pass 0 (steps 0-3) =================
+        floatx4 o[kHt][kPvColTiles];
+#pragma unroll
+        for (int mt = 0; mt < kHt; mt++)
+#pragma unroll
+            for (int i = 0; i < kPvColTiles; i++)
+                o[mt][i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        auto write_p = [&](int pass) {
+            PIPE_LANE
+#pragma unroll
+            for (int sp = 0; sp < kStepsPerPass; sp++)
+                *(u32x2 *)(pbuf + hl * kPRowBytes + 2 * (kStep * sp + 8 * g + 4 * par)) =
+                    pk[pass * kStepsPerPass + sp];
+        };
+        auto pv_pass = [&](int pass) {
+            PIPE_LANE
+            const int kp = n16 >> 1;
+            const int trrow = (kp < 4) ? 4 * g + kp : 16 + 4 * g + (kp - 4);
+#pragma unroll
+            for (int sp = 0; sp < kStepsPerPass; sp++) {
+                const uint8_t *tb = ring + (pass * kStepsPerPass + sp) * kTileBytes;
+                v2i raw[kPvColTiles];
+#pragma unroll
+                for (int i = 0; i < kPvColTiles; i++)
+                    raw[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (lds_v2i *)(tb + tile_off(trrow, kPvColTiles * wave + i) + 8 * (n16 & 1)));
+                bf16x8 pa[kHt];
+#pragma unroll
+                for (int mt = 0; mt < kHt; mt++)
+                    pa[mt] = as_bf16x8(*(const u32x4 *)(pbuf + (mt * 16 + n16) * kPRowBytes +
+                                                        2 * (kStep * sp + 8 * g)));
+#pragma unroll
+                for (int i = 0; i < kPvColTiles; i++) {
+                    const bf16x8 va = fp8x8_to_bf16x8(raw[i]);
+#pragma unroll
+                    for (int mt = 0; mt < kHt; mt++)
+                        o[mt][i] = mfma16x16x32(va, pa[mt], o[mt][i]);
+                }
+            }
+        };
+        // ================= the next unit: page lookups =================
+        // (in flight through the first P.V pass; the copies need them after it)
+        const bool more = finish_b();
+        // the next unit's query, into the registers this unit's QK is done with
+        // (unless the next unit is a chunk of the same row and head group)
+        if (more && (nr != cr || nhg != chg))
+            issue_q(qr);
+        write_p(0);
+        lds_barrier(); // P of pass 0 and every tile sum
+        pv_pass(0);
+        // page lookups and query retired before the copies go out (a wait for
+        // the query after them would also wait for the copies)
+        __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+        lds_barrier(); // pass 0's ring and P reads are done
+        if (more && wave < kStepsPerPass)
+            issue_tile();
+        write_p(1);
+        lds_barrier(); // P of pass 1
+        pv_pass(1);
+        lds_barrier(); // pass 1's ring reads are done
+        if (more && wave >= kStepsPerPass)
+            issue_tile();
+        // l of each head: the token-tile sums in tile order (read here, at
+        // their use: the next unit rewrites them only after its QK)
+        float lh[kHt];
+        {
+        PIPE_LANE
+#pragma unroll
+        for (int mt = 0; mt < kHt; mt++) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < kTokTiles; tt++)
+                acc += tsum[tt][16 * mt + n16];
+            lh[mt] = acc;
+        }
+        }
+
+        // ================= this unit becomes the previous one =================
+        have_prev = true;
+        pr = cr;
+        phg = chg;
+        pc = cc;
+        pnch = cnch;
+        pm = m;
+        plh = lh[ht];
+#pragma unroll
+        for (int mt = 0; mt < kHt; mt++) {
+            const float sc = (cnch == 1) ? (lh[mt] > 0.0f ? kv_scale / lh[mt] : 0.0f) : 1.0f;
+#pragma unroll
+            for (int i = 0; i < kPvColTiles; i++) {
+                pw[mt][i].x = pack_bf16x2(o[mt][i][0] * sc, o[mt][i][1] * sc);
+                pw[mt][i].y = pack_bf16x2(o[mt][i][2] * sc, o[mt][i][3] * sc);
+            }
+        }
+        if (!more)
+            break;
+        cu = nu;
+        cr = nr;
+        chg = nhg;
+        cc = nc;
+        cnch = nnch;
+    }
+    store_prev(0, kHt);
+#undef PIPE_LANE
+}
+
 // Fold the per-chunk partials of every (row, head): one wave per head,
 // kMergeHeads heads per workgroup, 8 latent columns per lane (the (m, l)
 // pairs of a head are wave-uniform loads).
@@ -584,12 +1043,23 @@ int launch_mla_decode(const LaunchShape &ls, const uint16_t *q, const uint8_t *k
     else if (units * ((ls.num_heads + 31) / 32) <= device_cus())
         G = 32;
     const int hgc = (ls.num_heads + G - 1) / G;
-    const dim3 grid(nch_max * hgc, ls.num_rows);
-    auto kern = G == 16 ? k_mla_decode<16> : G == 32 ? k_mla_decode<32> : k_mla_decode<kAttHeads>;
-    hipExtLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, t_att.start, t_att.stop, 0u, q,
-                          kv_cache, block_tables, seq_lens, sel, part_o, part_ml, out,
-                          ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size, ls.max_blocks,
-                          ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max, hgc);
+    const int cus = device_cus();
+    if (G == kAttHeads && units * hgc > cus) {
+        // more units than CUs: one workgroup per CU walks its units in turn
+        // (the same results; the next unit's copies overlap this one's work)
+        hipExtLaunchKernelGGL(k_mla_decode_pipe, dim3(cus), dim3(kAttThreads), 0, stream, t_att.start,
+                              t_att.stop, 0u, q, kv_cache, block_tables, seq_lens, sel, part_o, part_ml,
+                              out, ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size, ls.max_blocks,
+                              ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max, hgc,
+                              (int)(units * hgc));
+    } else {
+        const dim3 grid(nch_max * hgc, ls.num_rows);
+        auto kern = G == 16 ? k_mla_decode<16> : G == 32 ? k_mla_decode<32> : k_mla_decode<kAttHeads>;
+        hipExtLaunchKernelGGL(kern, grid, dim3(kAttThreads), 0, stream, t_att.start, t_att.stop, 0u, q,
+                              kv_cache, block_tables, seq_lens, sel, part_o, part_ml, out,
+                              ls.rows_per_seq, ls.num_heads, ls.top_k, ls.page_size, ls.max_blocks,
+                              ls.num_pages, ls.max_len, kv_scale, qk_log2, nch_max, hgc);
+    }
     if (hipGetLastError() != hipSuccess)
         return -1;
     if (nch_max > 1) {
