@@ -506,8 +506,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 // stays in registers), so that the ring never idles between units. While
 // unit u runs its softmax and P.V, the next unit's length and selected ids
 // are requested, and its tile copies go out as P.V frees the ring (steps 0-3
-// after the first P.V pass, 4-7 after the second); its QK then runs over step
-// pairs as they land, and unit u's output is stored during that QK. QK ownership: wave w scores token tile
+// after the first P.V pass, 4-7 after the second); unit u's output is stored
+// during the next unit's QK. QK ownership: wave w scores token tile
 // 2 st + (w & 1) of every step st for head tile w >> 1 (two waves a head
 // tile, as in k_mla_decode<64>). Every element's arithmetic is k_mla_decode's
 // (the same MFMA chains, maxima, exponentials, tile sums, P rounding and P.V
@@ -749,26 +749,24 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
     };
 
     for (;;) {
-        // ================= QK over step pairs as they land =================
+        // ================= QK over step pairs =================
         floatx4 z[kMaxSteps]; // z[st]: token tile 2 st + par, head hl
 #pragma unroll
         for (int p = 0; p < kMaxSteps / 2; p++) {
             PIPE_LANE
-            if ((wave >> 1) == p) // waves 2p, 2p + 1 copied steps 2p, 2p + 1
+            if (p == 0) {
+                // every wave's copies landed (each waits for its own step),
+                // then one barrier: one per step pair costs more than scoring
+                // the first pairs while the last land saves (measured)
                 __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
-            __asm__ volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            __asm__ volatile("" ::: "memory");
-            // the previous unit's output, head tile mt stored in pair
-            // max(mt, w >> 1): never before this wave's own tile wait (a store
-            // issued earlier would hold that wait)
-            if (have_prev) {
-                const int q0 = wave >> 1;
-                if (p == q0)
-                    store_prev(0, p + 1);
-                else if (p > q0)
-                    store_prev(p, p + 1);
+                __asm__ volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                __asm__ volatile("" ::: "memory");
             }
+            // the previous unit's output, head tile p in pair p: after the
+            // copy wait (a store issued before it would hold that wait)
+            if (have_prev)
+                store_prev(p, p + 1);
             floatx4 acc[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
             // the FP8 operands of four k-steps of both steps; the next group's
             // are requested before this group's conversions and products
