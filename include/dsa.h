@@ -144,7 +144,7 @@ int dsa_index_scores(const dsa_shape *shape, const void *q_idx, const float *w,
  * that holds whole rows; longer rows take a threshold filter and a finish
  * (two kernels). The result is the same unique top-k either way.
  */
-#define DSA_SELECT_DIRECT_MAX 8192
+#define DSA_SELECT_DIRECT_MAX 24576
 int dsa_topk_select(const dsa_shape *shape, const float *scores, const int32_t *seq_lens,
                     int32_t *sel, void *ws, size_t ws_bytes, void *stream);
 

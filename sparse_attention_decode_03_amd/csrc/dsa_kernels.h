@@ -80,10 +80,12 @@ int launch_index_scores(const LaunchShape &ls, const uint16_t *q_idx, const floa
                         uint32_t *gm4, uint32_t *gm32, hipStream_t stream, KTimer t = {});
 // Rows of at most kSelDirectMax tokens (by the shape's max_len) are
 // selected by one kernel that holds the whole row (no group maxima needed);
-// longer ones by the threshold filter and the finish.
-// (Measured: up to 8192 tokens one kernel wins, 22 us against 16 for the
-// two kernels at 64 rows x 16384; the whole-row histograms contend.)
-constexpr int kSelDirectMax = 8192;
+// longer ones by the threshold filter and the finish. The one kernel costs
+// more per row as rows grow (8.6 us at 8 tokens a thread, 13.4 at 16, 18.9
+// at 24, 21.8 at 32), the two kernels about 16-17 us whatever the length,
+// but the one kernel also spares the index pass its group maxima (2.6 us at
+// 64 rows x 16.4k) and a kernel boundary: it wins up to 24 tokens a thread.
+constexpr int kSelDirectMax = 24576;
 inline bool select_direct(const LaunchShape &ls) { return ls.max_len <= kSelDirectMax; }
 // have_group_max: the group maxima in the workspace were written by the
 // index pass of the same call; otherwise the selection computes them first

@@ -984,8 +984,13 @@ int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq
         for (hipEvent_t e : {t_filter.start, t_filter.stop})
             if (e != nullptr && hipEventRecord(e, stream) != hipSuccess)
                 return -1;
-        static_assert(kSelDirectMax <= 8 * kFinThreads, "eight tokens a thread");
-        hipExtLaunchKernelGGL(k_select_direct<8>, dim3(ls.num_rows), dim3(kFinThreads), 0, stream, t_finish.start,
+        // tokens a thread: the row length over the threads, rounded up to a
+        // multiple of 4 (float4 loads), at least 8
+        static_assert(kSelDirectMax <= 24 * kFinThreads, "at most 24 tokens a thread");
+        const int run = ls.max_len <= 8 * kFinThreads ? 8 : 4 * ((ls.max_len + 4 * kFinThreads - 1) / (4 * kFinThreads));
+        auto kern = run == 8 ? k_select_direct<8> : run == 12 ? k_select_direct<12>
+                  : run == 16 ? k_select_direct<16> : run == 20 ? k_select_direct<20> : k_select_direct<24>;
+        hipExtLaunchKernelGGL(kern, dim3(ls.num_rows), dim3(kFinThreads), 0, stream, t_finish.start,
                               t_finish.stop, 0u, scores, seq_lens, sel, ls.max_len, stride, ls.top_k);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }

@@ -25,7 +25,7 @@ DSA_EMETADATA = -6
 DSA_META_DEVICE = 0
 DSA_META_HOST = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20
-SELECT_DIRECT_MAX = 8192  # DSA_SELECT_DIRECT_MAX: one-kernel selection up to this max_len
+SELECT_DIRECT_MAX = 24576  # DSA_SELECT_DIRECT_MAX: one-kernel selection up to this max_len
 
 # Every symbol include/dsa.h declares.
 EXPORTS = (

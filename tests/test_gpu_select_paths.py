@@ -4,10 +4,11 @@ under (score descending, index ascending) (glm5next_dsa/layer.rs source page:
 `select_row`, and the doc of the prefill row-group selector before
 `batch_select_enabled`).
 
-Three launch shapes for the threshold filter and the finish: rows up to
-131072 tokens, rows past it (more slices than the others), and a top_k past
-2048; and three for the one-kernel selection of rows of at most 8192 tokens
-(DSA_SELECT_DIRECT_MAX), where the whole row is held and cut exactly (the
+Four launch shapes for the threshold filter and the finish: rows up to
+131072 tokens, rows past it (more slices than the others), a top_k past
+2048, and rows one token past the one-kernel cap; and seven for the
+one-kernel selection of rows of at most 24576 tokens (DSA_SELECT_DIRECT_MAX),
+where the whole row is held, 8 to 24 tokens a thread, and cut exactly (the
 same rows clamped to that length: all-equal, few levels, ramps, signed
 zeros, ties at the cut). The rows (tests/select_rows.py)
 reach these routes, as the CPU model of the selector confirms
@@ -37,6 +38,11 @@ ROUTES = {
     "8192 tokens, one kernel": (8192, 2048),
     "8192 tokens, top_k 100, one kernel": (8192, 100),
     "6000 tokens, one kernel": (6000, 2048),
+    "12000 tokens, one kernel (12 a thread)": (12000, 2048),
+    "16384 tokens, one kernel (16 a thread)": (16384, 2048),
+    "16388 tokens, one kernel (20 a thread)": (16388, 2048),
+    "24576 tokens, one kernel (24 a thread)": (24576, 2048),
+    "24577 tokens": (24577, 2048),
 }
 
 
