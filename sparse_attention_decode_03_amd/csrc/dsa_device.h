@@ -162,6 +162,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
                max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
                    (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
+// Sum over the wave, the same in every lane (after each step every lane of a
+// group holds the group's sum, so the mirror steps add disjoint halves).
+__device__ __forceinline__ float wave_total_f32(float x)
+{
+    x += __uint_as_float(dpp_u32<kDppQuadXor1>(__float_as_uint(x)));
+    x += __uint_as_float(dpp_u32<kDppQuadXor2>(__float_as_uint(x)));
+    x += __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(x)));
+    x += __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(x)));
+    const int b = __float_as_int(x);
+    return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 {
     v = min(v, dpp_u32<kDppQuadXor1>(v));

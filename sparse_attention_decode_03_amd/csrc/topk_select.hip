@@ -64,6 +64,7 @@ constexpr int kRankList = 256;              // boundary-bin members ranked direc
 struct BinSearch {
     uint32_t scan[kRowWaves + 1];
     uint32_t red[2][kRowWaves];
+    float fsum[kRowWaves]; // block_minmax_sum's partial sums
     uint32_t bin;
     uint32_t before;
     uint32_t total; // count of the last histogram walked by find_bin_desc_wave0
@@ -128,6 +129,31 @@ __device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, BinSear
     for (int w = 0; w < NW; w++) {
         lo = min(lo, bs->red[0][w]);
         hi = max(hi, bs->red[1][w]);
+    }
+}
+
+// block_minmax that also sums a float over the block, under the same
+// barrier (waves' partials added in wave order: deterministic).
+template <int NT>
+__device__ __forceinline__ void block_minmax_sum(uint32_t &lo, uint32_t &hi, float &x, BinSearch *bs)
+{
+    constexpr int NW = NT / kWave;
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    x = wave_total_f32(x);
+    const int wid = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        bs->red[0][wid] = lo;
+        bs->red[1][wid] = hi;
+        bs->fsum[wid] = x;
+    }
+    __syncthreads();
+    x = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        lo = min(lo, bs->red[0][w]);
+        hi = max(hi, bs->red[1][w]);
+        x += bs->fsum[w];
     }
 }
 
@@ -563,11 +589,12 @@ __device__ __forceinline__ void select_row_full(const float *__restrict__ scores
 // and ccount zero, both published by a barrier. Returns false, having
 // written nothing, when fewer than top_k candidates are held (the same
 // answer in every thread).
-template <int N>
+template <int N, bool VALUE_ANY = false>
 __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const uint32_t (&id)[N],
                                                 uint32_t valid, uint32_t lo, uint32_t hi,
                                                 int top_k, int32_t *out, uint8_t *area,
-                                                BinSearch &bs, uint32_t &ccount)
+                                                BinSearch &bs, uint32_t &ccount,
+                                                float vmean = 0.0f)
 {
     static_assert(N <= 32, "one mask bit per held candidate");
     const int tid = threadIdx.x;
@@ -590,11 +617,23 @@ __device__ __forceinline__ bool exact_cut_write(const uint32_t (&kk)[N], const u
     // decreases with the key, so the bins above the boundary bin are taken,
     // those below are not, and the boundary bin's members form one key
     // interval that the key passes below narrow.
-    if (lo < 0x80000000u && hi >= 0x80000000u) {
+    // With VALUE_ANY (a whole row held), keys on one side of zero take the
+    // value pass too when it pays: for a row whose values spread over their
+    // span (a bell, a plateau) the key image piles them into a few bins as
+    // well (measured, a 16k-token row of non-negative scores: 18.0 -> 13.6
+    // us), but a heavy tail's outliers set the span and leave nearly every
+    // value in the lowest value bins. The mean's place in the span tells the
+    // two apart (a heavy tail's mean sits near its bottom); vmean is the
+    // held values' mean, from the caller's range reduction.
+    const bool straddle = lo < 0x80000000u && hi >= 0x80000000u;
+    if (straddle || VALUE_ANY) {
         const float vlo = key_value(lo);
         const float span = key_value(hi) - vlo;
         const float scale = (float)kSelBins / span;
-        if (span > 0.0f && __builtin_isfinite(span) && __builtin_isfinite(scale)) {
+        bool use = span > 0.0f && __builtin_isfinite(span) && __builtin_isfinite(scale);
+        if (VALUE_ANY && !straddle && use)
+            use = 16.0f * (vmean - vlo) >= span;
+        if (use) {
             auto vbin = [&](uint32_t k) {
                 return (uint32_t)fminf((key_value(k) - vlo) * scale, (float)(kSelBins - 1));
             };
@@ -949,6 +988,7 @@ __global__ __launch_bounds__(kFinThreads) void k_select_direct(const float *__re
         v[q] = (t0 + 4 * q < L) ? *(const floatx4 *)(srow + t0 + 4 * q)
                                 : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t valid = 0u, lo = 0xFFFFFFFFu, hi = 0u;
+    float vsum = 0.0f; // the row's values summed for their mean (see exact_cut_write)
 #pragma unroll
     for (int j = 0; j < RUN; j++) {
         kk[j] = score_key(v[j / 4][j % 4]);
@@ -957,16 +997,18 @@ __global__ __launch_bounds__(kFinThreads) void k_select_direct(const float *__re
             valid |= 1u << j;
             lo = min(lo, kk[j]);
             hi = max(hi, kk[j]);
+            vsum += v[j / 4][j % 4];
         }
     }
     for (int i = tid; i < 2 * kSelHistWords; i += kFinThreads)
         ((uint32_t *)area)[i] = 0u;
     if (tid == 0)
         ccount = 0u;
-    block_minmax<kFinThreads>(lo, hi, &bs); // its barrier publishes the cleared bins
+    block_minmax_sum<kFinThreads>(lo, hi, vsum, &bs); // its barrier publishes the cleared bins
     // every token of the row is a candidate, so the first window holds
     // L > top_k of them and the cut never reports a shortfall
-    (void)exact_cut_write<RUN>(kk, id, valid, lo, hi, top_k, out, area, bs, ccount);
+    (void)exact_cut_write<RUN, true>(kk, id, valid, lo, hi, top_k, out, area, bs, ccount,
+                                     vsum / (float)L);
 }
 
 int launch_select(const LaunchShape &ls, const float *scores, const int32_t *seq_lens,

@@ -79,4 +79,10 @@ def crafted_rows(max_len: int, top_k: int):
     Lc = min(n, 131072)
     for name, vals in crafted_cut_rows(Lc, top_k).items():
         add(name, Lc, vals)
+    # non-negative rows (index scores are, when the head weights are): a bell
+    # spread over its span, and a heavy tail whose outliers set the span (the
+    # one-kernel cut bins the first by value, the second by key digits)
+    rng2 = np.random.default_rng(2025)
+    add("non-negative bell", n, (2.0 * np.abs(rng2.standard_normal(n))).astype(np.float32))
+    add("non-negative heavy tail", n, np.abs(rng2.standard_cauchy(n)).astype(np.float32))
     return rows

@@ -46,11 +46,16 @@ def key_values(keys: np.ndarray) -> np.ndarray:
     return u.view(np.float32)
 
 
-def value_bins(keys: np.ndarray, lo: int, hi: int):
+def value_bins(keys: np.ndarray, lo: int, hi: int, value_any: bool = False):
     """The kernels' value-linear bins in fp32, or None when the key range
     [lo, hi] does not straddle zero (or its value span is not finite):
-    bin = min(4095, floor((value - value(lo)) * (4096 / span)))."""
-    if not (lo < 0x80000000 <= hi):
+    bin = min(4095, floor((value - value(lo)) * (4096 / span))). With
+    value_any (the one-kernel cut over a whole row) a range on one side of
+    zero is binned by value too when the values' mean lies at least 1/16 of
+    the way up their span (the kernel decides in fp32; here in fp64, which
+    agrees away from that boundary)."""
+    straddle = lo < 0x80000000 <= hi
+    if not (straddle or value_any):
         return None
     with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
         vlo = key_values(np.array([lo], np.uint32))[0]
@@ -58,6 +63,10 @@ def value_bins(keys: np.ndarray, lo: int, hi: int):
         scale = np.float32(np.float32(BINS) / span)
         if not (span > 0 and np.isfinite(span) and np.isfinite(scale)):
             return None
+        if not straddle:
+            rel = key_values(keys).astype(np.float64) - np.float64(vlo)
+            if not 16.0 * rel.sum() >= len(keys) * np.float64(span):
+                return None
         x = np.float32(key_values(keys) - vlo) * scale
     return np.minimum(x.astype(np.float32), np.float32(BINS - 1)).astype(np.int64)
 
@@ -100,7 +109,8 @@ def threshold(keys: np.ndarray, top_k: int):
     return lo + (b << shift), level
 
 
-def exact_cut(kk: np.ndarray, ids: np.ndarray, top_k: int, window_only: bool = True):
+def exact_cut(kk: np.ndarray, ids: np.ndarray, top_k: int, window_only: bool = True,
+              value_any: bool = False):
     """The finishing workgroup's cut over candidates (kk, ids) in ascending id
     order. Returns (selected ids ascending, route details): the passes, whether
     a narrowed window was below 12 bits, and how the boundary bin was ranked
@@ -111,7 +121,7 @@ def exact_cut(kk: np.ndarray, ids: np.ndarray, top_k: int, window_only: bool = T
     narrow = False
     pre = np.zeros(len(kk), bool)     # taken by the value pass
     valid = np.ones(len(kk), bool)
-    vb = value_bins(kk.astype(np.uint32), int(kk.min()), int(kk.max()))
+    vb = value_bins(kk.astype(np.uint32), int(kk.min()), int(kk.max()), value_any)
     if vb is not None:
         b, before, total = walk_desc(np.bincount(vb, minlength=BINS), need)
         passes += 1
@@ -248,3 +258,31 @@ def test_gpu_route_rows_cover_every_route():
             "by slice", "spread", "member list", "equal keys", "narrowed below 12 bits",
             "value-bin first cut pass"}
     assert want <= seen, f"routes not reached: {sorted(want - seen)}"
+
+
+# The one-kernel launch shapes of the GPU route test (max_len, top_k).
+GPU_DIRECT_SHAPES = [(8192, 2048), (8192, 100), (6000, 2048), (12000, 2048), (16384, 2048),
+                     (16388, 2048), (24576, 2048)]
+
+
+def test_one_kernel_cut_rows_take_every_first_pass_and_are_exact():
+    """The one-kernel selection cuts a whole row: its crafted rows reach the
+    value-bin first pass across zero and on one side of it, and the key-digit
+    first pass for a heavy tail on one side of zero; every cut equals the
+    oracle's."""
+    seen = set()
+    for max_len, top_k in GPU_DIRECT_SHAPES:
+        for name, L, vals in crafted_rows(max_len, top_k):
+            if L <= top_k:
+                continue
+            row = vals[:L]
+            keys = order_keys(row)
+            sel, info = exact_cut(keys, np.arange(L), top_k, value_any=True)
+            np.testing.assert_array_equal(sel, oracle_ids(row, top_k),
+                                          err_msg=f"{name} ({max_len}, {top_k})")
+            across = int(keys.min()) < 0x80000000 <= int(keys.max())
+            seen.add(("value bins" if info["value_pass"] else "key digits")
+                     + (" across zero" if across else " on one side of zero"))
+    want = {"value bins across zero", "value bins on one side of zero",
+            "key digits on one side of zero"}
+    assert want <= seen, f"first passes not reached: {sorted(want - seen)}"
