@@ -28,7 +28,12 @@
 //     logit (log2 domain), p = exp2(z - m) rounded to bf16 for PV, and
 //     l = the 16 token-tile sums added in tile order (each tile sum in a
 //     fixed lane order). P goes to LDS in the PV operand's k order, 32 heads
-//     at a time.
+//     at a time. exp2 is the hardware exponential: for z - m >= -126 the
+//     same bits as the library's exp2f, which wraps it in a rescaling for
+//     subnormal results (five more instructions per value); below that p
+//     is flushed to zero, where exp2f gives a subnormal far under what the
+//     bf16 output resolves. A step whose every slot holds a selected token
+//     skips the mask.
 //  4. PV, transposed: O^T[latent col, head] += V^T P^T, the tile as A through
 //     the gfx950 8-bit transpose reads (ds_read_b64_tr_b8: a 16-lane group
 //     receives 8 token rows of one 16-column block) converted to bf16, P as
@@ -169,6 +174,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
     __shared__ float wmax[kAttWaves][16];       // per-wave maxima of its head tile's heads
     __shared__ float tsum[kTokTiles][G];        // per-token-tile sums of p
     __shared__ __align__(16) uint8_t vmask[kAttChunk]; // slot holds a selected token
+    __shared__ uint8_t vfull[kMaxSteps];                // every slot of step s does
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -248,6 +254,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
 
     if (lane < 32)
         vmask[slot] = row >= 0 ? 1 : 0;
+    if (lane == 0)
+        vfull[wave] = (__ballot(row >= 0) & 0xFFFFFFFFull) == 0xFFFFFFFFull ? 1 : 0;
     {
         uint8_t *tile = ring + wave * kTileBytes;
         // A skipped slot (past the chunk, or out of contract) copies one of
@@ -346,12 +354,21 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
                         a[h][k] = an[h][k];
             }
         }
+        // a step whose every slot holds a selected token needs no mask
+        if (__builtin_amdgcn_readfirstlane(vfull[tt >> 1])) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const uint32_t mw = *(const uint32_t *)(vmask + 16 * (tt + h) + 4 * g);
+            for (int h = 0; h < 2; h++)
 #pragma unroll
-            for (int v = 0; v < 4; v++)
-                z[j + h][v] = ((mw >> (8 * v)) & 0xFFu) ? acc[h][v] * qk_log2 : kNegInf;
+                for (int v = 0; v < 4; v++)
+                    z[j + h][v] = acc[h][v] * qk_log2;
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t mw = *(const uint32_t *)(vmask + 16 * (tt + h) + 4 * g);
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    z[j + h][v] = ((mw >> (8 * v)) & 0xFFu) ? acc[h][v] * qk_log2 : kNegInf;
+            }
         }
     }
     {
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode(
         for (int h = 0; h < 2; h++) {
 #pragma unroll
             for (int v = 0; v < 4; v++)
-                p[4 * h + v] = exp2f(z[j + h][v] - m_use);
+                p[4 * h + v] = __builtin_amdgcn_exp2f(z[j + h][v] - m_use);
             // tile sum: this lane's four tokens, then the four lane groups,
             // in one fixed order (the swaps add commuted pairs: same bits)
             float ts = (p[4 * h] + p[4 * h + 1]) + (p[4 * h + 2] + p[4 * h + 3]);
@@ -573,6 +590,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
     __shared__ float wmax[kAttWaves][16];
     __shared__ float tsum[kTokTiles][G];
     __shared__ __align__(16) uint8_t vmask[kAttChunk];
+    __shared__ uint8_t vfull[kMaxSteps];
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int ht = wave >> 1;  // QK head tile
@@ -659,6 +677,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
             vmask[slot] = row >= 0 ? 1 : 0;
         uint8_t *tile = ring + wave * kTileBytes;
         const uint64_t any = __ballot(row >= 0) & 0xFFFFFFFFull;
+        if (lane == 0)
+            vfull[wave] = any == 0xFFFFFFFFull ? 1 : 0;
         if (any != 0) {
             const int sub = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)any) - 1);
             const int src = row >= 0 ? row : sub;
@@ -802,11 +822,18 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
             }
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                const int tt = 2 * (2 * p + h) + par;
-                const uint32_t mw = *(const uint32_t *)(vmask + 16 * tt + 4 * g);
+                // a step whose every slot holds a selected token needs no mask
+                if (__builtin_amdgcn_readfirstlane(vfull[2 * p + h])) {
 #pragma unroll
-                for (int v = 0; v < 4; v++)
-                    z[2 * p + h][v] = ((mw >> (8 * v)) & 0xFFu) ? acc[h][v] * qk_log2 : kNegInf;
+                    for (int v = 0; v < 4; v++)
+                        z[2 * p + h][v] = acc[h][v] * qk_log2;
+                } else {
+                    const int tt = 2 * (2 * p + h) + par;
+                    const uint32_t mw = *(const uint32_t *)(vmask + 16 * tt + 4 * g);
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        z[2 * p + h][v] = ((mw >> (8 * v)) & 0xFFu) ? acc[h][v] * qk_log2 : kNegInf;
+                }
             }
         }
 
@@ -841,7 +868,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
             float p4[4];
 #pragma unroll
             for (int v = 0; v < 4; v++)
-                p4[v] = exp2f(z[st][v] - m_use);
+                p4[v] = __builtin_amdgcn_exp2f(z[st][v] - m_use);
             float ts = (p4[0] + p4[1]) + (p4[2] + p4[3]);
             ts = add_xor32(add_xor16(ts));
             if (g == 0)
