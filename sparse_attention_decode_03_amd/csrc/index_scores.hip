@@ -169,18 +169,23 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
         }
     }
     __syncthreads();
-    if (claim[0] < 0)
+    // the claim is the same for every lane: read into scalar registers, so
+    // that the key buffer's descriptor is scalar (a descriptor in vector
+    // registers makes the compiler wrap every load in a loop over its
+    // distinct values) and the tile loop branches on scalars
+    const int unit = __builtin_amdgcn_readfirstlane(claim[0]);
+    if (unit < 0)
         return; // past the last workgroup this split needs
-    const int s = claim[0] / RG;          // the unit's sequence
-    const int rbase = unit_row(claim[0]); // and its first row
+    const int s = unit / RG;          // the unit's sequence
+    const int rbase = unit_row(unit); // and its first row
     // the longest row of the unit: the tiles to score (from the claim, so
     // the first tile's loads go out with no further length load)
-    const int lmax = claim[3];
+    const int lmax = __builtin_amdgcn_readfirstlane(claim[3]);
     // tiles interleave across the sequence's workgroups (workgroup x takes
     // tiles x, x + W, x + 2W, ...), so at any moment the workgroups stream
     // neighbouring tiles and spread over every HBM channel
-    const int W = claim[2];
-    const int tile_first = claim[1];
+    const int W = __builtin_amdgcn_readfirstlane(claim[2]);
+    const int tile_first = __builtin_amdgcn_readfirstlane(claim[1]);
     const int tile_end = (lmax + TILE - 1) / TILE;
     if (tile_first >= tile_end)
         return;
@@ -348,7 +353,8 @@ __global__ __launch_bounds__(kIdxThreads, 2) void k_index_scores(
                 const int j = it / kBlocks;
                 const int blk = it % kBlocks;
                 const int r = rbase + j;
-                const int L = s_len[j]; // from LDS: no wait on the loads in flight
+                // from LDS (no wait on the loads in flight), into a scalar
+                const int L = __builtin_amdgcn_readfirstlane(s_len[j]);
                 if (t0 + blk * 32 >= L)
                     continue;
                 if (j != loaded) {
