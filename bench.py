@@ -159,8 +159,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by sequence with no exchange, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by sequence with no exchange between GPUs, so each GPU would run this "
+              "same step on its own sequences", file=sys.stderr)
         return 2
 
     import torch
