@@ -814,6 +814,16 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
     for (;;) {
         // ================= QK over step pairs =================
         floatx4 z[kMaxSteps]; // z[st]: token tile 2 st + par, head hl
+        // the lane's operand offset in a step tile for each of the 16
+        // k-steps: the same in every step, so that the four pairs' reads take
+        // it as their base and the steps' tile offsets as immediates
+        int qoff[16];
+        {
+            PIPE_LANE
+#pragma unroll
+            for (int kk = 0; kk < 16; kk++)
+                qoff[kk] = tile_off(16 * par + n16, 2 * kk + (g >> 1)) + 8 * (g & 1);
+        }
 #pragma unroll
         for (int p = 0; p < kMaxSteps / 2; p++) {
             PIPE_LANE
@@ -839,8 +849,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void k_mla_decode_pipe(
                     const uint8_t *tb = ring + (2 * p + h) * kTileBytes;
 #pragma unroll
                     for (int k = 0; k < 4; k++)
-                        a[h][k] = *(const v2i *)(tb + tile_off(16 * par + n16, 2 * (k0 + k) + (g >> 1)) +
-                                                 8 * (g & 1));
+                        a[h][k] = *(const v2i *)(tb + qoff[k0 + k]);
                 }
             };
             v2i a[2][4];
